@@ -1,0 +1,203 @@
+"""Plain fp64 definitions of the three attention cases — TEST INFRASTRUCTURE.
+
+This is the oracle the HIP kernels are checked against. It is deliberately
+slow and literal: every quantity is upcast losslessly to float64 (bf16 and
+float32 inputs are exact in float64) and the definitions are written out
+with NumPy primitives, with no blocking, fusion or reordering.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg use it. It shares no code with the HIP path.
+
+Sources (cited by page title and section):
+
+* [P1] "MiniCPM4 forward_step Attention Performance Fix" (VoxCPM issue 293):
+  §3 (the fix) passes only cache rows [0, position_id] to SDPA with no mask,
+  and argues this equals the lower-triangular mask and that position 0
+  reduces to the identity; §4.1 (patched ``forward_step``) gives the head
+  layout and ``enable_gqa=True``; §2.1/§2.3 give the original masked
+  full-cache form.
+* [P2] "step14_3 — batched attention: removing the per-head Python loop"
+  (mini-vllm tutorial): the problem section (per-head loop), the solution
+  section (bmm over heads, scale 1/sqrt(d_head), -inf mask, softmax, bmm)
+  and the "going further" section (SDPA with ``is_causal``).
+* [P3] "c2psa multi-head self-attention high-concurrency inference"
+  (blog post): core implementation §2 (dynamic top-k sparsification:
+  q·kᵀ, top-k per row, scatter into zeros, product with v) and the full
+  C2PSA class (topk=64 default, grouped heads).
+
+Readings where the pages are silent are listed in the design notes of the
+repository; the ones that shape this file are stated next to the code.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+
+def default_scale(D: int) -> float:
+    """1/sqrt(D): SDPA's default scale [P1 §4.1] and the explicit
+    ``/ math.sqrt(d_head)`` of [P2, solution section]."""
+    return 1.0 / math.sqrt(D)
+
+
+def _softmax(s: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis, max-subtracted (mathematically identical
+    to the unshifted form; -inf entries get weight exactly 0)."""
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+# ----------------------------------------------------------------------------
+# Decode  [P1 §3, §4.1]
+# ----------------------------------------------------------------------------
+def decode_sequence(q_b: np.ndarray, K_b: np.ndarray, V_b: np.ndarray,
+                    L: int, scale: float) -> np.ndarray:
+    """One sequence of a decode step.
+
+    q_b: [Hq, D]; K_b, V_b: [Hkv, >=L, D]. Query head h reads kv head
+    h // (Hq/Hkv) — consecutive query heads share a kv head, the grouping
+    ``enable_gqa=True`` performs [P1 §4.1]. Only rows [0, L) are read; the
+    slice bound is the causal mask [P1 §3]. L == 0 gives a zero row (reading:
+    the pages never reach it; a zero row rather than NaN).
+    """
+    Hq, D = q_b.shape
+    Hkv = K_b.shape[0]
+    G = Hq // Hkv
+    out = np.zeros((Hq, D), dtype=np.float64)
+    if L <= 0:
+        return out
+    for g in range(Hkv):
+        K = np.asarray(K_b[g, :L], dtype=np.float64)          # [L, D]
+        V = np.asarray(V_b[g, :L], dtype=np.float64)          # [L, D]
+        for h in range(g * G, (g + 1) * G):
+            qh = np.asarray(q_b[h], dtype=np.float64)          # [D]
+            s = scale * (K @ qh)                               # [L]
+            out[h] = _softmax(s) @ V                           # [D]
+    return out
+
+
+def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+           position_id: Optional[int] = None,
+           seq_lens: Optional[np.ndarray] = None,
+           scale: Optional[float] = None) -> np.ndarray:
+    """Single-token decode over a static cache.
+
+    q: [B, Hq, D]; k_cache, v_cache: [B, Hkv, max_length, D].
+    With ``position_id`` every sequence attends to rows [0, position_id]
+    (inclusive: the current token's K/V were written at ``position_id``
+    before attending [P1 §4.1]). With ``seq_lens`` sequence b attends to
+    rows [0, seq_lens[b]) clamped to [0, max_length].
+    Returns float64 [B, Hq, D].
+    """
+    B, Hq, D = q.shape
+    max_length = k_cache.shape[2]
+    if scale is None:
+        scale = default_scale(D)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        if seq_lens is None:
+            L = position_id + 1
+        else:
+            L = int(min(max(int(seq_lens[b]), 0), max_length))
+        out[b] = decode_sequence(q[b], k_cache[b], v_cache[b], L, scale)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Causal prefill against a cached prefix  [P2 solution section]
+# ----------------------------------------------------------------------------
+def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+            prefix_len: int, scale: Optional[float] = None) -> np.ndarray:
+    """Prefill of Lq new tokens whose K/V sit at cache rows
+    [prefix_len, prefix_len + Lq).
+
+    q: [B, Hq, Lq, D] (head-major, the SDPA convention of [P1 §4.1] and
+    [P2 going-further section]); caches [B, Hkv, max_length, D].
+    New token i attends to rows [0, prefix_len + i] (reading: the mask is
+    aligned to the bottom-right, so with prefix_len == 0 it is the ordinary
+    causal mask). For each head: scores = Q·Kᵀ·scale over all valid rows,
+    masked entries set to -inf, softmax per row, then ·V [P2 solution].
+    Returns float64 [B, Hq, Lq, D].
+    """
+    B, Hq, Lq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = default_scale(D)
+    T = prefix_len + Lq
+    i = np.arange(Lq)[:, None]
+    j = np.arange(T)[None, :]
+    masked = j > prefix_len + i                                # [Lq, T]
+    out = np.zeros((B, Hq, Lq, D), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            Q = np.asarray(q[b, h], dtype=np.float64)            # [Lq, D]
+            K = np.asarray(k_cache[b, g, :T], dtype=np.float64)  # [T, D]
+            V = np.asarray(v_cache[b, g, :T], dtype=np.float64)
+            s = (Q @ K.T) * scale                                # [Lq, T]
+            s = np.where(masked, -np.inf, s)
+            out[b, h] = _softmax(s) @ V
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Top-k sparsified scores  [P3 core implementation §2]
+# ----------------------------------------------------------------------------
+def topk_scores(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """s[i, j] = Σ_d q[i, d]·k[j, d] in float64, no scale [P3 §2].
+
+    q, k: [n, d] float32. Each product of two float32 values is exact in
+    float64; the sum runs over d in ascending order for every (i, j), so
+    identical key rows give bit-identical scores (needed for exact ties).
+    """
+    q64 = np.asarray(q, dtype=np.float64)
+    k64 = np.asarray(k, dtype=np.float64)
+    s = np.zeros((q64.shape[0], k64.shape[0]), dtype=np.float64)
+    for d in range(q64.shape[1]):
+        s += q64[:, d, None] * k64[None, :, d]
+    return s
+
+
+def topk_select(s: np.ndarray, topk: int) -> np.ndarray:
+    """Indices of the ``topk`` largest scores per row, ordered by (score
+    descending, index ascending) — ties go to the lower index (reading: the
+    page's ``torch.topk`` leaves equal scores unordered). Returned sorted
+    ascending per row. -0.0 and +0.0 compare equal here."""
+    order = np.argsort(-s, axis=-1, kind="stable")[:, :topk]
+    return np.sort(order, axis=-1)
+
+
+def topk_sparse(q: np.ndarray, k: np.ndarray, v: np.ndarray, topk: int,
+                return_details: bool = False):
+    """Top-k sparse attention [P3 §2]: scores q·kᵀ (no scale), keep the
+    ``topk`` largest per row, zero the rest, multiply by v. No softmax: the
+    page's code applies none (its prose says "before softmax" but the listed
+    function returns ``sparse_attn @ v`` directly; the code is followed).
+
+    q, k, v: [b, h, n, d] float32. Returns float64 [b, h, n, d], and with
+    ``return_details`` also the selected indices [b, h, n, topk] (ascending)
+    and the gap between the topk-th and (topk+1)-th largest scores per row
+    (+inf when topk == n).
+    """
+    bsz, H, n, d = q.shape
+    out = np.zeros((bsz, H, n, d), dtype=np.float64)
+    idx_all = np.zeros((bsz, H, n, topk), dtype=np.int64)
+    gap_all = np.full((bsz, H, n), np.inf, dtype=np.float64)
+    for b in range(bsz):
+        for h in range(H):
+            s = topk_scores(q[b, h], k[b, h])                    # [n, n]
+            idx = topk_select(s, topk)                           # [n, topk]
+            sel = np.take_along_axis(s, idx, axis=-1)            # [n, topk]
+            v64 = np.asarray(v[b, h], dtype=np.float64)          # [n, d]
+            out[b, h] = np.einsum("it,itd->id", sel, v64[idx])
+            idx_all[b, h] = idx
+            if topk < n:
+                srt = -np.sort(-s, axis=-1)
+                gap_all[b, h] = srt[:, topk - 1] - srt[:, topk]
+    if return_details:
+        return out, idx_all, gap_all
+    return out

@@ -1,0 +1,449 @@
+"""Pins for the fp64 oracle (CPU only).
+
+None of these re-types the oracle's formula. Each checks it against
+something fixed independently of it:
+
+* hand-worked examples from the pages' definitions (``tests/golden``);
+* closed forms (single row, uniform weights, constant V, k=1, k=n);
+* library routines the pages themselves call: PyTorch's CPU
+  ``scaled_dot_product_attention`` in float64 (sliced cache with
+  ``enable_gqa``, the original full-cache bool mask, ``is_causal``),
+  ``torch.topk`` + ``scatter`` and ``matmul``;
+* invariants the pages state (slice == mask, batched == per-head loop,
+  GQA == MHA with repeated K/V, position 0 == identity);
+* brute force over all k-subsets for top-k on tiny inputs.
+
+A plausible slip in the oracle (dropped scale, off-by-one length, wrong head
+map, transposed operand, softmax applied in top-k, wrong tie order) fails at
+least one test here.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+from conftest import GOLDEN
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+
+def _t(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float64))
+
+
+def _sdpa_sliced(q, k_cache, v_cache, L, scale=None):
+    """The pages' patched decode: SDPA over cache rows [0, L), enable_gqa."""
+    qt = _t(q)[:, :, None, :]                       # [B, Hq, 1, D]
+    kt = _t(k_cache[:, :, :L, :])
+    vt = _t(v_cache[:, :, :L, :])
+    o = F.scaled_dot_product_attention(qt, kt, vt, enable_gqa=True,
+                                       scale=scale)
+    return o[:, :, 0, :].numpy()
+
+
+# ----------------------------------------------------------------------------
+# Golden hand-worked examples
+# ----------------------------------------------------------------------------
+def test_decode_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "decode_hand.json")))
+    q = np.array(g["q"])
+    max_len = g["max_length"]
+    D = q.shape[-1]
+    k = np.full((1, 1, max_len, D), np.nan)
+    v = np.full((1, 1, max_len, D), np.nan)
+    n = len(g["k_rows"])
+    k[0, 0, :n] = g["k_rows"]
+    v[0, 0, :n] = g["v_rows"]
+    out = oracle.decode(q, k, v, position_id=g["position_id"])
+    np.testing.assert_allclose(out, np.array(g["expected"]),
+                               rtol=0, atol=g["tolerance"])
+
+
+def test_prefill_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "prefill_hand.json")))
+    q = np.array(g["q"])
+    k = np.array(g["k_rows"])[None, None]
+    v = np.array(g["v_rows"])[None, None]
+    out = oracle.prefill(q, k, v, prefix_len=g["prefix_len"])
+    np.testing.assert_allclose(out, np.array(g["expected"]),
+                               rtol=0, atol=g["tolerance"])
+
+
+def test_topk_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "topk_hand.json")))
+    q = np.array(g["q"], np.float32)
+    k = np.array(g["k"], np.float32)
+    v = np.array(g["v"], np.float32)
+    for case in g["cases"]:
+        out, idx, _ = oracle.topk_sparse(q, k, v, case["topk"],
+                                         return_details=True)
+        rows = case["rows"]
+        np.testing.assert_allclose(out[0, 0, rows], np.array(case["expected"]),
+                                   rtol=0, atol=g["tolerance"])
+        assert idx[0, 0, rows].tolist() == case["indices"]
+
+
+# ----------------------------------------------------------------------------
+# Decode
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_position0_returns_v0_exactly(dtype):
+    inp = synth.decode_uniform(11, B=2, Hq=8, Hkv=2, D=64, max_length=16,
+                               position_id=0, dtype=dtype)
+    q = synth.as_f32(inp.q, dtype)
+    k = synth.as_f32(inp.k_cache, dtype)
+    v = synth.as_f32(inp.v_cache, dtype)
+    out = oracle.decode(q, k, v, position_id=0)
+    expect = np.repeat(v[:, :, 0, :], 4, axis=1).astype(np.float64)
+    assert np.array_equal(out, expect)
+
+
+def test_decode_zero_query_gives_mean_of_valid_rows():
+    # q = 0 makes every score 0, so the weights are uniform over exactly the
+    # valid rows: an off-by-one in the length shows as a different mean.
+    rng = np.random.default_rng(0)
+    B, Hq, Hkv, D, M = 1, 4, 2, 8, 20
+    k = rng.standard_normal((B, Hkv, M, D))
+    v = rng.standard_normal((B, Hkv, M, D))
+    q = np.zeros((B, Hq, D))
+    for p in (0, 1, 7, 19):
+        out = oracle.decode(q, k, v, position_id=p)
+        mean = v[:, :, :p + 1, :].mean(axis=2)
+        np.testing.assert_allclose(out, np.repeat(mean, 2, axis=1),
+                                   rtol=0, atol=1e-14)
+
+
+def test_decode_constant_v_rows_sum_to_one():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((2, 6, 16)) * 3
+    k = rng.standard_normal((2, 3, 40, 16)) * 3
+    v = np.full((2, 3, 40, 16), 2.5)
+    out = oracle.decode(q, k, v, seq_lens=np.array([40, 5]))
+    np.testing.assert_allclose(out, 2.5, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,M,p", [
+    (1, 2, 1, 64, 32, 15), (2, 32, 8, 128, 64, 40), (1, 4, 4, 8, 9, 8),
+    (3, 6, 2, 16, 10, 0)])
+def test_decode_matches_torch_sdpa_on_sliced_cache(B, Hq, Hkv, D, M, p):
+    rng = np.random.default_rng(B * 1000 + p)
+    q = rng.standard_normal((B, Hq, D))
+    k = rng.standard_normal((B, Hkv, M, D))
+    v = rng.standard_normal((B, Hkv, M, D))
+    out = oracle.decode(q, k, v, position_id=p)
+    ref = _sdpa_sliced(q, k, v, p + 1)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    # an explicit scale is honoured, not replaced by the default
+    out2 = oracle.decode(q, k, v, position_id=p, scale=0.37)
+    ref2 = _sdpa_sliced(q, k, v, p + 1, scale=0.37)
+    np.testing.assert_allclose(out2, ref2, rtol=0, atol=1e-12)
+
+
+def test_decode_sliced_equals_masked_full_cache():
+    # The page's original form: full cache, bool mask arange(max) <= pos.
+    rng = np.random.default_rng(2)
+    B, Hq, Hkv, D, M = 2, 8, 2, 32, 50
+    q = rng.standard_normal((B, Hq, D))
+    k = rng.standard_normal((B, Hkv, M, D))
+    v = rng.standard_normal((B, Hkv, M, D))
+    for p in (0, 13, 49):
+        mask = (torch.arange(M) <= p)[None, :]   # [1 query, max_length]
+        ref = F.scaled_dot_product_attention(
+            _t(q)[:, :, None], _t(k), _t(v), attn_mask=mask,
+            enable_gqa=True)[:, :, 0].numpy()
+        out = oracle.decode(q, k, v, position_id=p)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_decode_gqa_equals_mha_with_repeated_kv():
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, D, M = 2, 12, 3, 16, 30
+    q = rng.standard_normal((B, Hq, D))
+    k = rng.standard_normal((B, Hkv, M, D))
+    v = rng.standard_normal((B, Hkv, M, D))
+    kr = torch.repeat_interleave(_t(k), Hq // Hkv, dim=1).numpy()
+    vr = torch.repeat_interleave(_t(v), Hq // Hkv, dim=1).numpy()
+    lens = np.array([30, 11])
+    np.testing.assert_allclose(oracle.decode(q, k, v, seq_lens=lens),
+                               oracle.decode(q, kr, vr, seq_lens=lens),
+                               rtol=0, atol=1e-14)
+
+
+def test_decode_ragged_equals_per_sequence_sdpa():
+    rng = np.random.default_rng(4)
+    B, Hq, Hkv, D, M = 4, 8, 4, 32, 33
+    q = rng.standard_normal((B, Hq, D))
+    k = rng.standard_normal((B, Hkv, M, D))
+    v = rng.standard_normal((B, Hkv, M, D))
+    lens = np.array([1, 33, 17, 2])
+    out = oracle.decode(q, k, v, seq_lens=lens)
+    for b in range(B):
+        ref = _sdpa_sliced(q[b:b + 1], k[b:b + 1], v[b:b + 1], lens[b])
+        np.testing.assert_allclose(out[b:b + 1], ref, rtol=0, atol=1e-12)
+
+
+def test_decode_length_zero_and_clamp():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((3, 2, 8))
+    k = rng.standard_normal((3, 1, 6, 8))
+    v = rng.standard_normal((3, 1, 6, 8))
+    out = oracle.decode(q, k, v, seq_lens=np.array([0, 100, -4]))
+    assert np.all(out[0] == 0) and np.all(out[2] == 0)
+    ref = _sdpa_sliced(q[1:2], k[1:2], v[1:2], 6)
+    np.testing.assert_allclose(out[1:2], ref, rtol=0, atol=1e-12)
+
+
+def test_decode_two_row_logistic_closed_form():
+    # L = 2: weights are the logistic function of the score difference.
+    rng = np.random.default_rng(6)
+    D = 16
+    q = rng.standard_normal((1, 1, D))
+    k = rng.standard_normal((1, 1, 2, D))
+    v = rng.standard_normal((1, 1, 2, D))
+    s = (k[0, 0] @ q[0, 0]) / math.sqrt(D)
+    w0 = 1.0 / (1.0 + math.exp(s[1] - s[0]))
+    expect = w0 * v[0, 0, 0] + (1 - w0) * v[0, 0, 1]
+    out = oracle.decode(q, k, v, position_id=1)
+    np.testing.assert_allclose(out[0, 0], expect, rtol=0, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# Prefill
+# ----------------------------------------------------------------------------
+def _bottom_right_mask(Lq, prefix):
+    i = torch.arange(Lq)[:, None]
+    j = torch.arange(prefix + Lq)[None, :]
+    return j <= prefix + i
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,Lq,prefix", [
+    (1, 4, 4, 16, 7, 9), (2, 8, 2, 32, 33, 0), (1, 2, 1, 8, 1, 20),
+    (1, 16, 16, 64, 40, 64)])
+def test_prefill_matches_torch_sdpa_bottom_right_mask(B, Hq, Hkv, D, Lq,
+                                                      prefix):
+    rng = np.random.default_rng(Lq * 100 + prefix)
+    T = prefix + Lq
+    q = rng.standard_normal((B, Hq, Lq, D))
+    k = rng.standard_normal((B, Hkv, T + 3, D))
+    v = rng.standard_normal((B, Hkv, T + 3, D))
+    out = oracle.prefill(q, k, v, prefix_len=prefix)
+    ref = F.scaled_dot_product_attention(
+        _t(q), _t(k[:, :, :T]), _t(v[:, :, :T]),
+        attn_mask=_bottom_right_mask(Lq, prefix), enable_gqa=True).numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_prefix0_equals_is_causal():
+    # The going-further section's SDPA call with is_causal=True is exact
+    # when there is no prefix.
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 4, 24, 16))
+    k = rng.standard_normal((1, 4, 24, 16))
+    v = rng.standard_normal((1, 4, 24, 16))
+    ref = F.scaled_dot_product_attention(_t(q), _t(k), _t(v),
+                                         is_causal=True).numpy()
+    np.testing.assert_allclose(oracle.prefill(q, k, v, 0), ref,
+                               rtol=0, atol=1e-12)
+
+
+def test_prefill_row_equals_decode_at_prefix_plus_i():
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, D, Lq, prefix = 2, 8, 4, 16, 5, 11
+    q = rng.standard_normal((B, Hq, Lq, D))
+    k = rng.standard_normal((B, Hkv, prefix + Lq, D))
+    v = rng.standard_normal((B, Hkv, prefix + Lq, D))
+    out = oracle.prefill(q, k, v, prefix)
+    for i in range(Lq):
+        dec = oracle.decode(q[:, :, i], k, v, position_id=prefix + i)
+        np.testing.assert_allclose(out[:, :, i], dec, rtol=0, atol=1e-14)
+
+
+def test_prefill_equals_per_head_loop_token_major():
+    # The problem section's per-head loop over token-major tensors
+    # Q [seq, H, d], K_full/V_full [total, H, d], joined with torch.cat.
+    rng = np.random.default_rng(9)
+    H, d, Lq, prefix = 6, 16, 9, 13
+    T = prefix + Lq
+    Q = _t(rng.standard_normal((Lq, H, d)))
+    Kf = _t(rng.standard_normal((T, H, d)))
+    Vf = _t(rng.standard_normal((T, H, d)))
+    mask = ~_bottom_right_mask(Lq, prefix)
+    outs = []
+    for h in range(H):
+        sc = torch.matmul(Q[:, h, :], Kf[:, h, :].T) / math.sqrt(d)
+        sc = sc.masked_fill(mask, float("-inf"))
+        outs.append(torch.matmul(torch.softmax(sc, dim=-1), Vf[:, h, :]))
+    ref = torch.cat(outs, dim=-1).numpy()                  # [Lq, H*d]
+    out = oracle.prefill(Q.transpose(0, 1)[None].numpy(),
+                         Kf.transpose(0, 1)[None].numpy(),
+                         Vf.transpose(0, 1)[None].numpy(), prefix)
+    out_tm = out[0].transpose(1, 0, 2).reshape(Lq, H * d)
+    np.testing.assert_allclose(out_tm, ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_never_reads_past_new_tokens():
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((1, 2, 4, 8))
+    k = rng.standard_normal((1, 2, 12, 8))
+    v = rng.standard_normal((1, 2, 12, 8))
+    k[:, :, 7:] = np.nan
+    v[:, :, 7:] = np.nan
+    out = oracle.prefill(q, k, v, prefix_len=3)
+    assert np.all(np.isfinite(out))
+
+
+# ----------------------------------------------------------------------------
+# Top-k
+# ----------------------------------------------------------------------------
+def test_topk_k_equals_n_is_dense_product_without_softmax():
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((2, 3, 20, 8)).astype(np.float32)
+    k = rng.standard_normal((2, 3, 20, 8)).astype(np.float32)
+    v = rng.standard_normal((2, 3, 20, 8)).astype(np.float32)
+    out = oracle.topk_sparse(q, k, v, 20)
+    qt, kt, vt = _t(q), _t(k), _t(v)
+    ref = torch.matmul(torch.matmul(qt, kt.transpose(-2, -1)), vt).numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-11)
+
+
+def test_topk_k1_is_max_score_times_argmax_row():
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((1, 2, 16, 8)).astype(np.float32)
+    k = rng.standard_normal((1, 2, 16, 8)).astype(np.float32)
+    v = rng.standard_normal((1, 2, 16, 8)).astype(np.float32)
+    out = oracle.topk_sparse(q, k, v, 1)
+    s = torch.matmul(_t(q), _t(k).transpose(-2, -1))
+    smax, arg = s.max(dim=-1)
+    ref = smax[..., None] * torch.gather(
+        _t(v), 2, arg[..., None].expand(-1, -1, -1, 8))
+    np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_topk_matches_page_topk_scatter_form():
+    # The page's code, with torch.topk + zeros_like.scatter + matmul, on
+    # data without ties (torch.topk's order among equal scores is unfixed).
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((2, 3, 64, 16)).astype(np.float32)
+    k = rng.standard_normal((2, 3, 64, 16)).astype(np.float32)
+    v = rng.standard_normal((2, 3, 64, 16)).astype(np.float32)
+    attn = torch.matmul(_t(q), _t(k).transpose(-2, -1))
+    val, idx = torch.topk(attn, k=10, dim=-1)
+    sparse = torch.zeros_like(attn).scatter(-1, idx, val)
+    ref = torch.matmul(sparse, _t(v)).numpy()
+    out, myidx, _ = oracle.topk_sparse(q, k, v, 10, return_details=True)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-11)
+    assert np.array_equal(np.sort(idx.numpy(), axis=-1), myidx)
+
+
+def test_topk_brute_force_over_all_subsets():
+    # The top-k set is the k-subset with the largest score sum; among equal
+    # sums the lexicographically smallest sorted index tuple (lower indices
+    # win ties). Enumerate every subset.
+    rng = np.random.default_rng(15)
+    n, d = 8, 3
+    for trial in range(6):
+        q = rng.integers(-3, 4, (1, 1, n, d)).astype(np.float32)
+        k = rng.integers(-3, 4, (1, 1, n, d)).astype(np.float32)
+        v = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+        for topk in (1, 3, 5, 8):
+            out, idx, _ = oracle.topk_sparse(q, k, v, topk,
+                                             return_details=True)
+            for i in range(n):
+                s = [float(np.dot(q[0, 0, i].astype(np.float64),
+                                  k[0, 0, j].astype(np.float64)))
+                     for j in range(n)]
+                best = None
+                for sub in itertools.combinations(range(n), topk):
+                    key = tuple(sorted((-s[j], j) for j in sub))
+                    if best is None or key < best[0]:
+                        best = (key, sub)
+                assert tuple(idx[0, 0, i]) == best[1]
+                expect = sum(s[j] * v[0, 0, j].astype(np.float64)
+                             for j in best[1])
+                np.testing.assert_allclose(out[0, 0, i], expect, rtol=0,
+                                           atol=1e-12)
+
+
+def test_topk_exact_ties_go_to_lower_index():
+    rng = np.random.default_rng(16)
+    n, d = 32, 8
+    q = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    k = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    k[0, 0, 20] = k[0, 0, 3]          # keys 3 and 20 tie for every query
+    k[0, 0, 27] = k[0, 0, 3]
+    v = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+    s = oracle.topk_scores(q[0, 0], k[0, 0])
+    assert np.array_equal(s[:, 3], s[:, 20]) and np.array_equal(s[:, 3],
+                                                                s[:, 27])
+    for topk in range(1, n + 1):
+        _, idx, _ = oracle.topk_sparse(q, k, v, topk, return_details=True)
+        for i in range(n):
+            sel = set(idx[0, 0, i].tolist())
+            # whenever a later copy is in, every earlier copy is in too
+            if 27 in sel:
+                assert 20 in sel and 3 in sel
+            if 20 in sel:
+                assert 3 in sel
+
+
+def test_topk_zero_query_selects_first_indices():
+    q = np.zeros((1, 1, 4, 8), np.float32)
+    rng = np.random.default_rng(17)
+    k = rng.standard_normal((1, 1, 4, 8)).astype(np.float32)
+    k[0, 0, 1] *= -1  # negative zero products appear
+    v = rng.standard_normal((1, 1, 4, 8)).astype(np.float32)
+    out, idx, _ = oracle.topk_sparse(q, k, v, 2, return_details=True)
+    assert idx[0, 0].tolist() == [[0, 1]] * 4
+    assert np.all(out == 0)
+
+
+@pytest.mark.slow
+def test_fp32_accumulation_is_not_enough_for_topk_tolerance():
+    # Why the kernel accumulates top-k scores and outputs in fp64: on the
+    # C2PSA shape an fp32-accumulated path misses the 1e-4 fp32 tolerance.
+    inp = synth.topk(5, 4, 3, 512, 64, 64)
+    q, k, v = (torch.from_numpy(x) for x in (inp.q, inp.k, inp.v))
+    attn = torch.matmul(q, k.transpose(-2, -1))
+    val, idx = torch.topk(attn, k=64, dim=-1)
+    sparse = torch.zeros_like(attn).scatter(-1, idx, val)
+    out32 = torch.matmul(sparse, v).double().numpy()
+    ref = oracle.topk_sparse(inp.q, inp.k, inp.v, 64)
+    assert np.max(np.abs(out32 - ref)) > 1e-4
+    # while rounding the exact result to fp32 alone stays well inside it
+    assert np.max(np.abs(ref.astype(np.float32).astype(np.float64) - ref)) \
+        < 5e-5
+
+
+# ----------------------------------------------------------------------------
+# Input generators (not the oracle, but both sides depend on them)
+# ----------------------------------------------------------------------------
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal(100000).astype(np.float32) * 10
+    x[:4] = [0.0, -0.0, 1e-40, -3.4e38]
+    bits = synth.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(bits.view(np.int16), ref)
+    back = synth.bf16_to_f32(bits)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16)
+                          .float().numpy())
+
+
+def test_generators_are_seeded_and_poisoned():
+    a = synth.decode_uniform(2, 1, 4, 2, 16, 10, 3, "bf16")
+    b = synth.decode_uniform(2, 1, 4, 2, 16, 10, 3, "bf16")
+    assert np.array_equal(a.k_cache, b.k_cache)
+    kf = synth.bf16_to_f32(a.k_cache)
+    assert np.all(np.isnan(kf[:, :, 4:])) and np.all(np.isfinite(kf[:, :, :4]))
+    r = synth.decode_ragged(3, 4, 4, 2, 16, 12, "f32")
+    for bb in range(4):
+        L = r.seq_lens[bb]
+        assert np.all(np.isfinite(r.k_cache[bb, :, :L]))
+        assert np.all(np.isnan(r.k_cache[bb, :, L:]))
