@@ -1,0 +1,172 @@
+/*
+ * attn.h — C ABI of the MI355X (gfx950) KV-cache attention library.
+ *
+ * Three operations, each one asynchronous launch sequence on the caller's
+ * HIP stream:
+ *
+ *   attn_decode   single-token decode over a statically preallocated cache,
+ *                 attending to rows [0, position_id] (or [0, seq_lens[b]) for
+ *                 a ragged batch) with no materialised mask.
+ *                 Source: "MiniCPM4 forward_step Attention Performance Fix",
+ *                 §3 (pass only the valid cache rows; the slice bound is the
+ *                 causal mask) and §4.1 (patched forward_step: SDPA with
+ *                 enable_gqa over the sliced cache, default scale).
+ *   attn_prefill  causal prefill of Lq new tokens against a cached prefix,
+ *                 every head in one launch.
+ *                 Source: "step14_3 — batched attention: removing the per-head
+ *                 Python loop", solution section (all heads at once: Q·Kᵀ
+ *                 scaled by 1/sqrt(d_head), causal -inf mask, softmax, ·V) and
+ *                 the going-further section (one fused kernel).
+ *   attn_topk     top-k sparsified scores: q·kᵀ with no scale, keep the
+ *                 topk largest per row, zero the rest, multiply by v; no
+ *                 softmax.
+ *                 Source: "c2psa multi-head self-attention high-concurrency
+ *                 inference", core implementation §2 (dynamic top-k
+ *                 sparsification) and the full C2PSA class (topk=64).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers (memory the caller allocated with hipMalloc
+ *   or through a framework) unless stated otherwise. The caller owns every
+ *   buffer. The library allocates nothing, keeps no pointer after the call
+ *   returns and never synchronises; results are valid once the caller has
+ *   synchronised `stream`.
+ * - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ * - Layouts are dense, row-major, innermost dimension contiguous. Data
+ *   pointers must be 16-byte aligned. `out` must not alias an input.
+ * - Every argument check is done on host scalars before any launch; a failed
+ *   check launches nothing and returns a nonzero status. `attn_last_error()`
+ *   then describes the failing argument (per thread).
+ * - Device faults are sticky HIP errors: they surface as ATTN_E_HIP on this
+ *   or a later call and the process must restart.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_E_ARG = 1,         /* invalid argument (null pointer, bad size, ...) */
+  ATTN_E_UNSUPPORTED = 2, /* valid, but outside the supported set          */
+  ATTN_E_WORKSPACE = 3,   /* workspace missing or too small                */
+  ATTN_E_HIP = 4          /* a HIP launch or runtime call failed           */
+} attn_status;
+
+typedef enum attn_dtype {
+  ATTN_F32 = 0,  /* IEEE binary32                                          */
+  ATTN_BF16 = 1  /* bfloat16 (upper 16 bits of binary32)                    */
+} attn_dtype;
+
+/* Static description of a status code. Never NULL. */
+const char *attn_status_str(int status);
+
+/* Human-readable reason for the last nonzero status returned on the calling
+ * thread ("" if none). Valid until the next call on the same thread. */
+const char *attn_last_error(void);
+
+/* ABI version, bumped on any signature or semantic change. */
+int attn_abi_version(void);
+
+/* --------------------------------------------------------------------------
+ * Decode
+ * --------------------------------------------------------------------------
+ * Workspace bytes attn_decode needs for these sizes. `split_rows` is the same
+ * value later passed to attn_decode (0 = automatic choice). The result is an
+ * upper bound valid for every position_id / seq_lens. Returns 0 for invalid
+ * sizes. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D,
+                                   int max_length, int split_rows);
+
+/* out[b,h,:] = softmax_j(scale * q[b,h,:]·K[b,g,j,:]) · V[b,g,j,:] over the
+ * valid rows j of sequence b, where g = h / (Hq/Hkv) (consecutive query heads
+ * share one kv head, as enable_gqa does).
+ *
+ *   dtype      ATTN_F32 or ATTN_BF16; q, caches and out all use it. Scores,
+ *              softmax and accumulation are fp32; bf16 output is rounded to
+ *              nearest even.
+ *   q          [B][Hq][D]
+ *   k_cache,
+ *   v_cache    [B][Hkv][max_length][D]; max_length is the token stride, so
+ *              passing the whole cache plus position_id is the zero-copy form
+ *              of slicing it to rows [0, position_id]. Rows past the valid
+ *              length are never read (they may hold anything, NaN included).
+ *              The current token's K/V must already be stored at its row.
+ *   out        [B][Hq][D] (the same memory as [B][Hq*D]).
+ *   position_id  used when seq_lens == NULL: every sequence attends to rows
+ *              [0, position_id]; requires 0 <= position_id < max_length.
+ *   seq_lens   optional DEVICE array int32[B]: sequence b attends to rows
+ *              [0, seq_lens[b]). Values are clamped to [0, max_length] on the
+ *              device; length 0 yields a zero output row.
+ *   scale      multiplier of q·k; any finite value (the Python binding
+ *              passes 1/sqrt(D) when the caller gives none).
+ *   split_rows cache rows per split-KV work item (0 = automatic). Forcing it
+ *              changes only the reduction order, never the math.
+ *   workspace  device scratch of at least
+ *              attn_decode_workspace_bytes(B,Hq,Hkv,D,max_length,split_rows)
+ *              bytes, 256-byte aligned; no initial contents required. Its
+ *              contents are undefined after the call. Concurrent calls need
+ *              distinct workspaces.
+ * Supported: D in {64, 128}; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8};
+ * B, Hkv <= 65535. B == 0 is a no-op. */
+int attn_decode(int dtype, const void *q, const void *k_cache,
+                const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
+                int max_length, int position_id, const int32_t *seq_lens,
+                float scale, int split_rows, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/* --------------------------------------------------------------------------
+ * Prefill
+ * --------------------------------------------------------------------------
+ * New token i (0 <= i < Lq) sits at cache row prefix_len + i and attends to
+ * rows [0, prefix_len + i] (the causal mask aligned to the bottom-right; with
+ * prefix_len == 0 it is the ordinary causal mask).
+ *
+ *   dtype      ATTN_BF16 (bf16 inputs, bf16 matrix cores, fp32 softmax and
+ *              accumulation, probabilities rounded to bf16 before ·V, bf16
+ *              output rounded to nearest even).
+ *   q          [B][Hq][Lq][D]
+ *   k_cache,
+ *   v_cache    [B][Hkv][max_length][D]; rows [0, prefix_len + Lq) must hold
+ *              the prefix and the new tokens' K/V; later rows are never read.
+ *   out        [B][Hq][Lq][D]
+ *   scale      any finite value (binding default 1/sqrt(D)).
+ * Requires 0 <= prefix_len, 0 <= Lq, prefix_len + Lq <= max_length.
+ * Supported: D in {64, 128}; Hq % Hkv == 0; B, Hq <= 65535. Lq == 0 or
+ * B == 0 is a no-op. */
+int attn_prefill(int dtype, const void *q, const void *k_cache,
+                 const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
+                 int max_length, int Lq, int prefix_len, float scale,
+                 void *stream);
+
+/* --------------------------------------------------------------------------
+ * Top-k sparse attention
+ * --------------------------------------------------------------------------
+ * For every row i of every (b, h): s_ij = Σ_d q[i,d]·k[j,d] (no scale), the
+ * set S_i = the topk indices j with the largest s_ij (equal scores: the lower
+ * index first), out[i,:] = Σ_{j∈S_i} s_ij · v[j,:]. Unselected j contribute
+ * exactly zero; no softmax.
+ *
+ * Scores and the output sum are accumulated in fp64 (every fp32·fp32 product
+ * is exact in fp64) and the selection is made on the fp64 scores; the output
+ * is rounded once to fp32.
+ *
+ *   q, k, v, out  fp32 [b][h][n][d]
+ *   idx_out       optional int32 [b][h][n][topk] (NULL to skip): the selected
+ *                 indices of each row in ascending order.
+ * Supported: d == 64; 1 <= n <= 1024; 1 <= topk <= n; b, h <= 65535.
+ * b == 0 is a no-op. */
+int attn_topk(const float *q, const float *k, const float *v, float *out,
+              int32_t *idx_out, int b, int h, int n, int d, int topk,
+              void *stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* ATTN_H */

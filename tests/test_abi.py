@@ -1,0 +1,200 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+``include/attn.h`` declares, and rejects every invalid argument with the
+documented status before any HIP call (fake, aligned device pointers are
+never dereferenced on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+tas = pytest.importorskip("transformer_attention_split_amd")
+lib = tas.lib
+
+HEADER = os.path.join(ROOT, "include", "attn.h")
+P = 0x10000          # fake 16-byte-aligned device pointer, never touched
+OK, E_ARG, E_UNSUP, E_WS, E_HIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for n in ("attn_decode", "attn_prefill", "attn_topk",
+              "attn_decode_workspace_bytes", "attn_status_str"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} not exported by libattn.so"
+    assert set(tas.EXPORTED) == set(declared_functions())
+
+
+def test_status_strings_and_version():
+    for s in range(5):
+        assert lib.attn_status_str(s).decode().startswith("ATTN_")
+    assert lib.attn_status_str(99).decode() == "unknown attn_status"
+    assert lib.attn_abi_version() == 1
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+def decode(**kw):
+    a = dict(dtype=BF16, q=P, k=P, v=P, out=P, B=1, Hq=32, Hkv=8, D=128,
+             max_length=8192, position_id=100, seq_lens=None, scale=0.088,
+             split_rows=0, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_decode(a["dtype"], a["q"], a["k"], a["v"], a["out"],
+                           a["B"], a["Hq"], a["Hkv"], a["D"],
+                           a["max_length"], a["position_id"], a["seq_lens"],
+                           a["scale"], a["split_rows"], a["ws"],
+                           a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), E_ARG),
+    (dict(B=-1), E_ARG),
+    (dict(B=70000), E_ARG),
+    (dict(Hq=0), E_ARG),
+    (dict(Hkv=0), E_ARG),
+    (dict(Hq=30, Hkv=8), E_ARG),
+    (dict(Hq=48, Hkv=3), E_UNSUP),      # group 16
+    (dict(Hq=24, Hkv=8), E_UNSUP),      # group 3
+    (dict(D=0), E_ARG),
+    (dict(D=96), E_UNSUP),
+    (dict(D=256), E_UNSUP),
+    (dict(max_length=0), E_ARG),
+    (dict(position_id=-1), E_ARG),
+    (dict(position_id=8192), E_ARG),
+    (dict(scale=float("nan")), E_ARG),
+    (dict(scale=float("inf")), E_ARG),
+    (dict(split_rows=-5), E_ARG),
+    (dict(q=None), E_ARG),
+    (dict(k=None), E_ARG),
+    (dict(v=None), E_ARG),
+    (dict(out=None), E_ARG),
+    (dict(q=P + 8), E_ARG),
+    (dict(k=P + 2), E_ARG),
+    (dict(out=P + 4), E_ARG),
+    (dict(seq_lens=P + 2), E_ARG),
+    (dict(ws=None), E_WS),
+    (dict(ws_bytes=16), E_WS),
+    (dict(ws=P + 16), E_WS),
+])
+def test_decode_rejects(kw, status):
+    assert decode(**kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_decode_seq_lens_path_ignores_position_id():
+    # With seq_lens given, position_id is not checked; the call fails only on
+    # the (deliberately) missing workspace, before any launch.
+    assert decode(seq_lens=P, position_id=-7, ws=None) == E_WS
+
+
+def test_decode_batch_zero_is_a_noop():
+    assert decode(B=0, ws=None, ws_bytes=0) == OK
+
+
+def test_decode_workspace_bound():
+    ws = lib.attn_decode_workspace_bytes
+    assert ws(0, 32, 8, 128, 8192, 0) == 0
+    assert ws(1, 32, 8, 128, 0, 0) == 0
+    a = ws(1, 32, 8, 128, 8192, 0)
+    assert a > 0 and a % 256 == 0
+    # explicit split rows: ceil(max_length / split_rows) splits
+    e = ws(2, 4, 2, 64, 1000, 100)
+    assert e >= 2 * 4 * 10 * (64 + 2) * 4
+    assert ws(2, 4, 2, 64, 1000, 1) > e
+
+
+# ----------------------------------------------------------------------------
+# prefill
+# ----------------------------------------------------------------------------
+def prefill(**kw):
+    a = dict(dtype=BF16, q=P, k=P, v=P, out=P, B=1, Hq=16, Hkv=16, D=64,
+             max_length=4096, Lq=1024, prefix_len=3072, scale=0.125,
+             stream=None)
+    a.update(kw)
+    return lib.attn_prefill(a["dtype"], a["q"], a["k"], a["v"], a["out"],
+                            a["B"], a["Hq"], a["Hkv"], a["D"],
+                            a["max_length"], a["Lq"], a["prefix_len"],
+                            a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), E_ARG),
+    (dict(dtype=F32), E_UNSUP),
+    (dict(B=-1), E_ARG),
+    (dict(Hq=0), E_ARG),
+    (dict(Hq=16, Hkv=3), E_ARG),
+    (dict(D=32), E_UNSUP),
+    (dict(D=-64), E_ARG),
+    (dict(Lq=-1), E_ARG),
+    (dict(prefix_len=-1), E_ARG),
+    (dict(prefix_len=3073), E_ARG),     # prefix + Lq > max_length
+    (dict(max_length=0), E_ARG),
+    (dict(scale=float("nan")), E_ARG),
+    (dict(q=None), E_ARG),
+    (dict(out=P + 2), E_ARG),
+])
+def test_prefill_rejects(kw, status):
+    assert prefill(**kw) == status
+
+
+def test_prefill_empty_is_a_noop():
+    assert prefill(Lq=0) == OK
+    assert prefill(B=0) == OK
+
+
+# ----------------------------------------------------------------------------
+# topk
+# ----------------------------------------------------------------------------
+def topk(**kw):
+    a = dict(q=P, k=P, v=P, out=P, idx=None, b=32, h=3, n=512, d=64, topk=64,
+             stream=None)
+    a.update(kw)
+    return lib.attn_topk(a["q"], a["k"], a["v"], a["out"], a["idx"], a["b"],
+                         a["h"], a["n"], a["d"], a["topk"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(b=-1), E_ARG),
+    (dict(h=70000), E_ARG),
+    (dict(d=0), E_ARG),
+    (dict(d=128), E_UNSUP),
+    (dict(n=0), E_ARG),
+    (dict(n=2048), E_UNSUP),
+    (dict(topk=0), E_ARG),
+    (dict(topk=513), E_ARG),
+    (dict(v=None), E_ARG),
+    (dict(k=P + 4), E_ARG),
+    (dict(idx=P + 2), E_ARG),
+])
+def test_topk_rejects(kw, status):
+    assert topk(**kw) == status
+
+
+def test_topk_empty_is_a_noop():
+    assert topk(b=0) == OK
+    assert topk(h=0) == OK
+
+
+def test_python_binding_raises_with_reason():
+    import torch
+    q = torch.zeros(1, 2, 64)  # CPU tensor: rejected by the binding
+    with pytest.raises(ValueError):
+        tas.attn_decode(q, torch.zeros(1, 1, 4, 64), torch.zeros(1, 1, 4, 64),
+                        position_id=0)
+    with pytest.raises(tas.AttnArgError) as ei:
+        tas._binding._check(E_UNSUP, "x")
+    assert "UNSUPPORTED" in str(ei.value)

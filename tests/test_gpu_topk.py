@@ -1,0 +1,124 @@
+"""GPU parity of attn_topk against the fp64 oracle.
+
+The selected index set is compared exactly wherever the oracle's gap between
+the topk-th and (topk+1)-th largest score exceeds what two fp64 summation
+orders can disagree by; in rows where it does not (expected: none on random
+data), the GPU's set only has to be a valid top-k set of the oracle scores.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import F32_TOL, max_abs_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+tas = pytest.importorskip("transformer_attention_split_amd")
+
+
+def run(q, k, v, topk):
+    qd, kd, vd = (to_dev(x, "f32") for x in (q, k, v))
+    b, h, n, _ = q.shape
+    idx = torch.empty(b, h, n, topk, dtype=torch.int32, device="cuda")
+    out = tas.attn_topk(qd, kd, vd, topk, idx_out=idx)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), idx.cpu().numpy()
+
+
+def check(q, k, v, topk, out, idx):
+    ref, ref_idx, gap = oracle.topk_sparse(q, k, v, topk, return_details=True)
+    b, h, n, _ = q.shape
+    ambiguous = 0
+    for bb in range(b):
+        for hh in range(h):
+            s = oracle.topk_scores(q[bb, hh], k[bb, hh])
+            eps = 1e-10 * (1.0 + np.max(np.abs(s), axis=-1))
+            amb = gap[bb, hh] <= eps
+            ambiguous += int(amb.sum())
+            got = idx[bb, hh]
+            # ascending, distinct, in range
+            assert np.all(np.diff(got, axis=-1) > 0) if topk > 1 else True
+            assert got.min() >= 0 and got.max() < n
+            clear = ~amb
+            assert np.array_equal(got[clear], ref_idx[bb, hh][clear])
+            for i in np.nonzero(amb)[0]:
+                sel = np.zeros(n, bool)
+                sel[got[i]] = True
+                if topk < n:
+                    assert s[i, sel].min() >= s[i, ~sel].max() - eps[i]
+                ref[bb, hh, i] = s[i, got[i]] @ v[bb, hh, got[i]].astype(
+                    np.float64)
+    err = max_abs_err(out, ref)
+    assert err <= F32_TOL, err
+    return ambiguous
+
+
+def test_topk_c2psa_full():
+    p = synth.WORKLOADS["topk_c2psa"].params
+    inp = synth.topk(p["seed"], p["b"], p["h"], p["n"], p["d"], p["topk"])
+    say("topk b=32 h=3 n=512 d=64 topk=64")
+    out, idx = run(inp.q, inp.k, inp.v, inp.topk)
+    amb = check(inp.q, inp.k, inp.v, inp.topk, out, idx)
+    assert amb == 0
+
+
+@pytest.mark.parametrize("n,topk", [
+    (1, 1), (5, 2), (16, 16), (63, 7), (64, 64), (65, 1), (100, 33),
+    (512, 512), (512, 1), (700, 64), (1024, 64), (1024, 1000)])
+def test_topk_sizes(n, topk):
+    inp = synth.topk(40 + n, 2, 2, n, 64, topk)
+    say(f"topk n={n} topk={topk}")
+    out, idx = run(inp.q, inp.k, inp.v, topk)
+    check(inp.q, inp.k, inp.v, topk, out, idx)
+
+
+def test_topk_k_equals_n_is_dense():
+    inp = synth.topk(50, 1, 3, 200, 64, 200)
+    say("topk k=n dense")
+    out, _ = run(inp.q, inp.k, inp.v, 200)
+    q, k, v = (x.astype(np.float64) for x in (inp.q, inp.k, inp.v))
+    ref = (q @ np.swapaxes(k, -1, -2)) @ v
+    assert max_abs_err(out, ref) <= F32_TOL
+
+
+def test_topk_exact_ties_lower_index_wins():
+    inp = synth.topk(51, 1, 2, 256, 64, 40)
+    k = inp.k.copy()
+    # many exact ties: copies of a few key rows scattered over the row
+    for j in range(0, 256, 7):
+        k[:, :, j] = k[:, :, 3]
+    k[:, :, 200:230] = k[:, :, 100:101]
+    say("topk exact ties")
+    for topk in (1, 10, 40, 37, 100):
+        out, idx = run(inp.q, k, inp.v, topk)
+        ref, ref_idx, _ = oracle.topk_sparse(inp.q, k, inp.v, topk,
+                                             return_details=True)
+        assert np.array_equal(idx, ref_idx), topk
+        assert max_abs_err(out, ref) <= F32_TOL
+
+
+def test_topk_zero_queries_and_signed_zeros():
+    inp = synth.topk(52, 1, 1, 130, 64, 9)
+    q = inp.q.copy()
+    q[0, 0, :20] = 0.0
+    q[0, 0, 20:25] = -0.0
+    say("topk zero queries")
+    out, idx = run(q, inp.k, inp.v, 9)
+    assert np.array_equal(idx[0, 0, :25],
+                          np.tile(np.arange(9), (25, 1)))
+    assert np.all(out[0, 0, :25] == 0)
+    check(q, inp.k, inp.v, 9, out, idx)
+
+
+def test_topk_repeatable_and_without_index_output():
+    inp = synth.topk(53, 2, 3, 512, 64, 64)
+    qd, kd, vd = (to_dev(x, "f32") for x in (inp.q, inp.k, inp.v))
+    say("topk repeatability")
+    a = tas.attn_topk(qd, kd, vd, 64)
+    b = tas.attn_topk(qd, kd, vd, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    out, _ = run(inp.q, inp.k, inp.v, 64)
+    assert np.array_equal(a.cpu().numpy().astype(np.float64), out)

@@ -1,0 +1,25 @@
+"""MI355X (gfx950) KV-cache attention: split-KV decode, causal prefill
+against a cached prefix, and top-k sparse scores, as hand-written HIP kernels
+behind a C ABI (``include/attn.h``). This package is the thin Python binding.
+"""
+from ._binding import (  # noqa: F401
+    ATTN_BF16,
+    ATTN_E_ARG,
+    ATTN_E_HIP,
+    ATTN_E_UNSUPPORTED,
+    ATTN_E_WORKSPACE,
+    ATTN_F32,
+    ATTN_OK,
+    EXPORTED,
+    LIB_PATH,
+    AttnArgError,
+    AttnError,
+    attn_decode,
+    attn_decode_workspace_bytes,
+    attn_prefill,
+    attn_topk,
+    lib,
+)
+
+__all__ = ["attn_decode", "attn_prefill", "attn_topk",
+           "attn_decode_workspace_bytes", "AttnError", "AttnArgError"]

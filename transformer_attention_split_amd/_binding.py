@@ -1,0 +1,233 @@
+"""ctypes binding of libattn.so.
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+shape, turned into device pointers and sizes, and handed to the C ABI on the
+caller's current stream. Every step of the computation runs in the HIP
+kernels; there is no fallback path. If the shared library is missing the
+import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_OK, ATTN_E_ARG, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = range(5)
+ATTN_F32, ATTN_BF16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with "
+        "`python -m transformer_attention_split_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+_f = ctypes.c_float
+
+lib.attn_status_str.restype = ctypes.c_char_p
+lib.attn_status_str.argtypes = [_i]
+lib.attn_last_error.restype = ctypes.c_char_p
+lib.attn_last_error.argtypes = []
+lib.attn_abi_version.restype = _i
+lib.attn_abi_version.argtypes = []
+lib.attn_decode_workspace_bytes.restype = _sz
+lib.attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+lib.attn_decode.restype = _i
+lib.attn_decode.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p,
+                            _f, _i, _p, _sz, _p]
+lib.attn_prefill.restype = _i
+lib.attn_prefill.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                             _f, _p]
+lib.attn_topk.restype = _i
+lib.attn_topk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+
+EXPORTED = ("attn_status_str", "attn_last_error", "attn_abi_version",
+            "attn_decode_workspace_bytes", "attn_decode", "attn_prefill",
+            "attn_topk")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.attn_status_str(status).decode()
+        detail = lib.attn_last_error().decode()
+        super().__init__(f"{where}: {msg}" + (f" — {detail}" if detail else ""))
+
+
+class AttnArgError(AttnError, ValueError):
+    pass
+
+
+def _check(status: int, where: str) -> None:
+    if status == ATTN_OK:
+        return
+    if status in (ATTN_E_ARG, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE):
+        raise AttnArgError(status, where)
+    raise AttnError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    h = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return h or None
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _need_dense(name: str, t: torch.Tensor, ndim: int) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ----------------------------------------------------------------------------
+# Decode
+# ----------------------------------------------------------------------------
+def attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int,
+                                max_length: int, split_rows: int = 0) -> int:
+    return int(lib.attn_decode_workspace_bytes(B, Hq, Hkv, D, max_length,
+                                               split_rows))
+
+
+def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                *, position_id: Optional[int] = None,
+                seq_lens: Optional[torch.Tensor] = None,
+                scale: Optional[float] = None, split_rows: int = 0,
+                out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """Single-token decode. q [B,Hq,D]; caches [B,Hkv,max_length,D];
+    exactly one of ``position_id`` (rows [0, position_id]) or ``seq_lens``
+    (int32 [B] on the GPU, rows [0, seq_lens[b])). Returns out [B,Hq,D]."""
+    _need_dense("q", q, 3)
+    _need_dense("k_cache", k_cache, 4)
+    _need_dense("v_cache", v_cache, 4)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, k_cache and v_cache must share one dtype")
+    B, Hq, D = q.shape
+    Bk, Hkv, max_length, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match "
+                         f"q {tuple(q.shape)}")
+    if (position_id is None) == (seq_lens is None):
+        raise ValueError("pass exactly one of position_id or seq_lens")
+    if seq_lens is not None:
+        _need_dense("seq_lens", seq_lens, 1)
+        if seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+            raise ValueError("seq_lens must be int32 [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_dense("out", out, 3)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q's shape and dtype")
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, D, max_length, split_rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8,
+                                device=q.device)
+    st = lib.attn_decode(_dtype_code(q), _ptr(q), _ptr(k_cache),
+                         _ptr(v_cache), _ptr(out), B, Hq, Hkv, D, max_length,
+                         -1 if position_id is None else int(position_id),
+                         _ptr(seq_lens), float(scale), int(split_rows),
+                         _ptr(workspace), workspace.numel(),
+                         _stream_handle(stream))
+    _check(st, "attn_decode")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Prefill
+# ----------------------------------------------------------------------------
+def attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 *, prefix_len: int, scale: Optional[float] = None,
+                 out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """Causal prefill. q [B,Hq,Lq,D] bf16; caches [B,Hkv,max_length,D] with
+    the new tokens' K/V at rows [prefix_len, prefix_len+Lq). Returns
+    out [B,Hq,Lq,D]."""
+    _need_dense("q", q, 4)
+    _need_dense("k_cache", k_cache, 4)
+    _need_dense("v_cache", v_cache, 4)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, k_cache and v_cache must share one dtype")
+    B, Hq, Lq, D = q.shape
+    Bk, Hkv, max_length, Dk = k_cache.shape
+    if Bk != B or Dk != D:
+        raise ValueError("cache shape does not match q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_dense("out", out, 4)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q's shape and dtype")
+    st = lib.attn_prefill(_dtype_code(q), _ptr(q), _ptr(k_cache),
+                          _ptr(v_cache), _ptr(out), B, Hq, Hkv, D, max_length,
+                          Lq, int(prefix_len), float(scale),
+                          _stream_handle(stream))
+    _check(st, "attn_prefill")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Top-k
+# ----------------------------------------------------------------------------
+def attn_topk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
+              *, out: Optional[torch.Tensor] = None,
+              idx_out: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """Top-k sparse attention. q, k, v float32 [b,h,n,d]. Returns out
+    [b,h,n,d]; if ``idx_out`` (int32 [b,h,n,topk]) is given it receives the
+    selected indices of each row in ascending order."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_dense(name, t, 4)
+        if t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k and v must share one shape")
+    b, h, n, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_dense("out", out, 4)
+        if out.shape != q.shape or out.dtype != torch.float32:
+            raise ValueError("out must be float32 of q's shape")
+    if idx_out is not None:
+        _need_dense("idx_out", idx_out, 4)
+        if idx_out.dtype != torch.int32 or \
+                tuple(idx_out.shape) != (b, h, n, topk):
+            raise ValueError("idx_out must be int32 [b,h,n,topk]")
+    st = lib.attn_topk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx_out),
+                       b, h, n, d, int(topk), _stream_handle(stream))
+    _check(st, "attn_topk")
+    return out

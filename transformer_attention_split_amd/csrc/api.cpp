@@ -1,0 +1,270 @@
+// C ABI layer: argument validation, split planning and kernel enqueue.
+//
+// Every check below runs on host scalars before any HIP call, so an invalid
+// call never touches the device. Nothing here allocates device memory or
+// synchronises a stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(ATTN_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void *p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Product of extents fits comfortably in a signed 64-bit byte offset.
+bool fits(std::initializer_list<double> dims) {
+  double p = 1.0;
+  for (double d : dims) p *= d;
+  return p < 4.0e18;
+}
+
+// ---------------------------------------------------------------------------
+// Decode planning. A work item is (split, kv head, sequence). The automatic
+// choice aims for about kTargetBlocks workgroups so every CU has several to
+// interleave, with at least kMinSplitRows rows per split so a workgroup's
+// 16-byte-per-lane loads stay deep enough to cover HBM latency.
+// ---------------------------------------------------------------------------
+constexpr long kTargetBlocks = 8192;
+constexpr int kMaxSplits = 1024;
+constexpr int kMinSplitRows = 128;
+constexpr int kRowQuantum = 64;
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+int auto_split_target(int B, int Hkv) {
+  long items = (long)B * Hkv;
+  long s = (kTargetBlocks + items - 1) / items;
+  if (s < 1) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return (int)s;
+}
+
+attn::DecodePlan plan_decode(int B, int Hkv, int L_bound, int split_rows) {
+  attn::DecodePlan p{};
+  if (split_rows > 0) {
+    p.split_rows = split_rows;
+  } else {
+    const int target = auto_split_target(B, Hkv);
+    int sr = ceil_div(L_bound, target);
+    sr = ceil_div(sr, kRowQuantum) * kRowQuantum;
+    if (sr < kMinSplitRows) sr = kMinSplitRows;
+    p.split_rows = sr;
+  }
+  p.splits = ceil_div(L_bound, p.split_rows);
+  if (p.splits < 1) p.splits = 1;
+  return p;
+}
+
+// Upper bound on splits for any valid length <= max_length.
+int max_splits(int B, int Hkv, int max_length, int split_rows) {
+  if (split_rows > 0) return ceil_div(max_length, split_rows);
+  int a = auto_split_target(B, Hkv);
+  int b = ceil_div(max_length, kMinSplitRows);
+  return a < b ? a : b;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t ws_ml_bytes(int B, int Hq, int S) {
+  return align256((size_t)B * Hq * S * 2 * sizeof(float));
+}
+size_t ws_o_bytes(int B, int Hq, int S, int D) {
+  return align256((size_t)B * Hq * S * D * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_E_ARG: return "ATTN_E_ARG: invalid argument";
+    case ATTN_E_UNSUPPORTED: return "ATTN_E_UNSUPPORTED: outside the supported set";
+    case ATTN_E_WORKSPACE: return "ATTN_E_WORKSPACE: workspace missing or too small";
+    case ATTN_E_HIP: return "ATTN_E_HIP: HIP runtime error";
+  }
+  return "unknown attn_status";
+}
+
+const char *attn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_abi_version(void) { return 1; }
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D,
+                                   int max_length, int split_rows) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || D < 1 || max_length < 1 || split_rows < 0)
+    return 0;
+  if (B == 0) return 0;
+  if (!fits({(double)B, (double)Hq, (double)max_length, (double)D}))
+    return 0;
+  const int S = max_splits(B, Hkv, max_length, split_rows);
+  return ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S, D);
+}
+
+int attn_decode(int dtype, const void *q, const void *k_cache,
+                const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
+                int max_length, int position_id, const int32_t *seq_lens,
+                float scale, int split_rows, void *workspace,
+                size_t workspace_bytes, void *stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_E_ARG, "attn_decode: unknown dtype %d", dtype);
+  if (B < 0 || B > 65535)
+    return fail(ATTN_E_ARG, "attn_decode: B=%d outside [0, 65535]", B);
+  if (Hq < 1 || Hkv < 1 || Hkv > 65535)
+    return fail(ATTN_E_ARG, "attn_decode: Hq=%d Hkv=%d must be >= 1 (Hkv <= 65535)", Hq, Hkv);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_E_ARG, "attn_decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(ATTN_E_UNSUPPORTED, "attn_decode: group size Hq/Hkv=%d not in {1,2,4,8}", G);
+  if (D < 1) return fail(ATTN_E_ARG, "attn_decode: D=%d", D);
+  if (D != 64 && D != 128)
+    return fail(ATTN_E_UNSUPPORTED, "attn_decode: D=%d not in {64,128}", D);
+  if (max_length < 1)
+    return fail(ATTN_E_ARG, "attn_decode: max_length=%d must be >= 1", max_length);
+  if (!fits({(double)B, (double)Hkv, (double)max_length, (double)D, 4.0}) ||
+      !fits({(double)B, (double)Hq, (double)max_length, (double)D, 4.0}))
+    return fail(ATTN_E_ARG, "attn_decode: cache extents overflow");
+  if (seq_lens == nullptr && (position_id < 0 || position_id >= max_length))
+    return fail(ATTN_E_ARG, "attn_decode: position_id=%d outside [0, max_length=%d)",
+                position_id, max_length);
+  if (!std::isfinite(scale))
+    return fail(ATTN_E_ARG, "attn_decode: scale is not finite");
+  if (split_rows < 0)
+    return fail(ATTN_E_ARG, "attn_decode: split_rows=%d < 0", split_rows);
+  if (B == 0) return ok();  // empty batch: nothing is read or written
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(ATTN_E_ARG, "attn_decode: null data pointer");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, 16))
+    return fail(ATTN_E_ARG, "attn_decode: data pointers must be 16-byte aligned");
+  if (seq_lens && !aligned(seq_lens, 4))
+    return fail(ATTN_E_ARG, "attn_decode: seq_lens must be 4-byte aligned");
+  const size_t need =
+      attn_decode_workspace_bytes(B, Hq, Hkv, D, max_length, split_rows);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(ATTN_E_WORKSPACE, "attn_decode: workspace %zu bytes, need %zu",
+                workspace ? workspace_bytes : (size_t)0, need);
+  if (!aligned(workspace, 256))
+    return fail(ATTN_E_WORKSPACE, "attn_decode: workspace must be 256-byte aligned");
+
+  const int L_bound = seq_lens ? max_length : position_id + 1;
+  attn::DecodeArgs a{};
+  a.bf16 = dtype == ATTN_BF16;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.out = out;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.max_length = max_length;
+  a.position_id = position_id;
+  a.seq_lens = seq_lens;
+  a.scale = scale;
+  a.plan = plan_decode(B, Hkv, L_bound, split_rows);
+  a.ws_ml = static_cast<float *>(workspace);
+  a.ws_o = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                     ws_ml_bytes(B, Hq, a.plan.splits));
+  hipError_t e = attn::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attn_decode launch");
+  return ok();
+}
+
+int attn_prefill(int dtype, const void *q, const void *k_cache,
+                 const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
+                 int max_length, int Lq, int prefix_len, float scale,
+                 void *stream) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_E_ARG, "attn_prefill: unknown dtype %d", dtype);
+  if (dtype != ATTN_BF16)
+    return fail(ATTN_E_UNSUPPORTED, "attn_prefill: only ATTN_BF16 is supported");
+  if (B < 0 || B > 65535)
+    return fail(ATTN_E_ARG, "attn_prefill: B=%d outside [0, 65535]", B);
+  if (Hq < 1 || Hq > 65535 || Hkv < 1)
+    return fail(ATTN_E_ARG, "attn_prefill: Hq=%d Hkv=%d must be >= 1 (Hq <= 65535)", Hq, Hkv);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_E_ARG, "attn_prefill: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (D < 1) return fail(ATTN_E_ARG, "attn_prefill: D=%d", D);
+  if (D != 64 && D != 128)
+    return fail(ATTN_E_UNSUPPORTED, "attn_prefill: D=%d not in {64,128}", D);
+  if (max_length < 1 || Lq < 0 || prefix_len < 0)
+    return fail(ATTN_E_ARG, "attn_prefill: max_length=%d Lq=%d prefix_len=%d",
+                max_length, Lq, prefix_len);
+  if ((long long)prefix_len + Lq > max_length)
+    return fail(ATTN_E_ARG, "attn_prefill: prefix_len+Lq=%lld exceeds max_length=%d",
+                (long long)prefix_len + Lq, max_length);
+  if (!fits({(double)B, (double)Hkv, (double)max_length, (double)D, 2.0}) ||
+      !fits({(double)B, (double)Hq, (double)max_length, (double)D, 2.0}))
+    return fail(ATTN_E_ARG, "attn_prefill: extents overflow");
+  if (!std::isfinite(scale))
+    return fail(ATTN_E_ARG, "attn_prefill: scale is not finite");
+  if (B == 0 || Lq == 0) return ok();  // nothing is read or written
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(ATTN_E_ARG, "attn_prefill: null data pointer");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, 16))
+    return fail(ATTN_E_ARG, "attn_prefill: data pointers must be 16-byte aligned");
+  attn::PrefillArgs a{q, k_cache, v_cache, out, B, Hq, Hkv, D, max_length,
+                      Lq, prefix_len, scale};
+  hipError_t e = attn::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attn_prefill launch");
+  return ok();
+}
+
+int attn_topk(const float *q, const float *k, const float *v, float *out,
+              int32_t *idx_out, int b, int h, int n, int d, int topk,
+              void *stream) {
+  if (b < 0 || b > 65535 || h < 0 || h > 65535)
+    return fail(ATTN_E_ARG, "attn_topk: b=%d h=%d outside [0, 65535]", b, h);
+  if (d < 1) return fail(ATTN_E_ARG, "attn_topk: d=%d", d);
+  if (d != 64) return fail(ATTN_E_UNSUPPORTED, "attn_topk: d=%d, only 64", d);
+  if (n < 1) return fail(ATTN_E_ARG, "attn_topk: n=%d must be >= 1", n);
+  if (n > 1024) return fail(ATTN_E_UNSUPPORTED, "attn_topk: n=%d > 1024", n);
+  if (topk < 1 || topk > n)
+    return fail(ATTN_E_ARG, "attn_topk: topk=%d outside [1, n=%d]", topk, n);
+  if (b == 0 || h == 0) return ok();  // nothing is read or written
+  if (!q || !k || !v || !out)
+    return fail(ATTN_E_ARG, "attn_topk: null data pointer");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(out, 16))
+    return fail(ATTN_E_ARG, "attn_topk: data pointers must be 16-byte aligned");
+  if (idx_out && !aligned(idx_out, 4))
+    return fail(ATTN_E_ARG, "attn_topk: idx_out must be 4-byte aligned");
+  attn::TopkArgs a{q, k, v, out, idx_out, b, h, n, d, topk};
+  hipError_t e = attn::launch_topk(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attn_topk launch");
+  return ok();
+}
+
+}  // extern "C"

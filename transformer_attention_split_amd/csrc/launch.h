@@ -1,0 +1,52 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the kernel
+// translation units. Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Threads per decode split workgroup.
+constexpr int kDecodeThreads = 256;
+
+struct DecodePlan {
+  int split_rows;  // cache rows per split work item
+  int splits;      // split work items per (b, kv head) in the grid
+};
+
+struct DecodeArgs {
+  bool bf16;
+  const void *q, *k, *v;
+  void *out;
+  int B, Hq, Hkv, D, max_length;
+  int position_id;          // used when seq_lens == nullptr
+  const int32_t *seq_lens;  // device, may be null
+  float scale;
+  DecodePlan plan;
+  float *ws_ml;  // [B][Hq][splits][2]  (running max, running sum)
+  float *ws_o;   // [B][Hq][splits][D]  (unnormalised output)
+};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  void *out;
+  int B, Hq, Hkv, D, max_length, Lq, prefix_len;
+  float scale;
+};
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+struct TopkArgs {
+  const float *q, *k, *v;
+  float *out;
+  int32_t *idx;
+  int b, h, n, d, topk;
+};
+
+hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,255 @@
+// Top-k sparsified attention scores (gfx950).
+//
+// Operation: "c2psa multi-head self-attention high-concurrency inference",
+// core implementation §2 — scores q·kᵀ with no scale, keep the topk largest
+// of every row, zero the others, multiply the sparse matrix by v; no softmax.
+// Equal scores at the boundary go to the lower key index.
+//
+// Precision: every fp32·fp32 product is exact in fp64, so scores and the
+// output sum are accumulated in fp64 and the selection is made on the fp64
+// scores; the output is rounded once to fp32.
+//
+// One workgroup = 4 waves = 16 query rows of one (b, h):
+//   1. scores: S[16][n] with v_mfma_f64_16x16x4_f64 (A = the 16 query rows,
+//      B = 16 key rows per block; the 64 dimensions are spread as 16 MFMAs of
+//      4), written to LDS. Waves take key blocks round-robin.
+//   2. select, one row per wave at a time, lane e holding keys e, e+64, ...:
+//      a) the k-th largest fp32-rounded score T by bisection over the 32-bit
+//         order-preserving key, counting with wave ballots; every score whose
+//         fp32 key exceeds T is in (rounding is monotone);
+//      b) only if more scores share T than places remain, the same bisection
+//         over the exact 64-bit keys of those candidates, and remaining ties
+//         are filled in ascending key index.
+//      The chosen (index, score) pairs are compacted in ascending index order
+//      (into the row's own LDS storage and a per-wave index list).
+//   3. gather: lanes = 4 slot groups x 16 groups of 4 dimensions; each slot
+//      group walks every 4th selected key and adds score * v[key] in fp64
+//      (one coalesced 256-byte row read per key per slot group); the four
+//      partial sums are added across lanes and rounded to fp32.
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int QB = 16;  // query rows per workgroup
+constexpr int DIM = 64;
+
+__device__ __forceinline__ uint32_t order32(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t order64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+template <int NTP>
+__global__ __launch_bounds__(kThreads) void topk_kernel(
+    const float *__restrict__ qg, const float *__restrict__ kg,
+    const float *__restrict__ vg, float *__restrict__ outg,
+    int32_t *__restrict__ idxg, int H, int n, int topk) {
+  constexpr int NP = 64 * NTP;  // padded row length
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  double *S = reinterpret_cast<double *>(smem);                 // [QB][NP]
+  int *jl = reinterpret_cast<int *>(smem + (size_t)QB * NP * 8);  // [4][NP]
+
+  const int q0 = blockIdx.x * QB;
+  const size_t bh = (size_t)blockIdx.z * H + blockIdx.y;
+  const float *qb = qg + bh * n * DIM;
+  const float *kb = kg + bh * n * DIM;
+  const float *vb = vg + bh * n * DIM;
+  const int tid = threadIdx.x;
+  const int w = tid / 64;
+  const int l = tid % 64;
+  const int li = l % 16;
+  const int lg = l / 16;
+
+  // ---- 1. scores ---------------------------------------------------------------
+  {
+    double qa[16];
+    {
+      const int qr = q0 + li;
+      float4 x[4] = {};
+      if (qr < n) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          x[c] = *reinterpret_cast<const float4 *>(qb + (size_t)qr * DIM + 16 * lg + 4 * c);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        qa[4 * c + 0] = x[c].x;
+        qa[4 * c + 1] = x[c].y;
+        qa[4 * c + 2] = x[c].z;
+        qa[4 * c + 3] = x[c].w;
+      }
+    }
+    const int nkb = (n + 15) / 16;
+    for (int blk = w; blk < nkb; blk += 4) {
+      const int kr = blk * 16 + li;
+      float4 x[4] = {};
+      if (kr < n) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          x[c] = *reinterpret_cast<const float4 *>(kb + (size_t)kr * DIM + 16 * lg + 4 * c);
+      }
+      f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 0], (double)x[c].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 1], (double)x[c].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 2], (double)x[c].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 3], (double)x[c].w, acc, 0, 0, 0);
+      }
+      // lane l, register r holds query row lg + 4r, key blk*16 + li
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[(lg + 4 * r) * NP + blk * 16 + li] = acc[r];
+    }
+  }
+  __syncthreads();
+
+  const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));  // lanes < l
+
+  for (int ii = 0; ii < 4; ++ii) {
+    const int i = 4 * w + ii;  // row inside the block
+    const int qr = q0 + i;
+    const bool row_ok = qr < n;  // uniform over the wave
+    if (row_ok) {
+      // ---- 2. select ---------------------------------------------------------------
+      double s[NTP];
+      uint32_t k32[NTP];
+#pragma unroll
+      for (int t = 0; t < NTP; ++t) {
+        const int j = l + 64 * t;
+        const bool ok = j < n;
+        s[t] = ok ? S[i * NP + j] + 0.0 : 0.0;  // +0.0 turns -0 into +0
+        k32[t] = ok ? order32((float)s[t] + 0.0f) : 0u;
+      }
+      uint32_t T = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int t = 0; t < NTP; ++t) cnt += __popcll(__ballot(k32[t] >= cand));
+        if (cnt >= topk) T = cand;
+      }
+      uint64_t selm[NTP], cm[NTP];
+      int gt = 0, nc = 0;
+#pragma unroll
+      for (int t = 0; t < NTP; ++t) {
+        selm[t] = __ballot(k32[t] > T);
+        cm[t] = __ballot(k32[t] == T);
+        gt += __popcll(selm[t]);
+        nc += __popcll(cm[t]);
+      }
+      const int need = topk - gt;  // >= 1
+      if (nc == need) {
+#pragma unroll
+        for (int t = 0; t < NTP; ++t) selm[t] |= cm[t];
+      } else {
+        // Exact fp64 order among the candidates sharing the fp32 key T.
+        uint64_t k64[NTP];
+#pragma unroll
+        for (int t = 0; t < NTP; ++t)
+          k64[t] = ((cm[t] >> l) & 1ull) ? order64(s[t]) : 0ull;
+        uint64_t T2 = 0;
+        for (int bit = 63; bit >= 0; --bit) {
+          const uint64_t cand = T2 | (1ull << bit);
+          int cnt = 0;
+#pragma unroll
+          for (int t = 0; t < NTP; ++t) cnt += __popcll(__ballot(k64[t] >= cand));
+          if (cnt >= need) T2 = cand;
+        }
+        int need2 = need;
+#pragma unroll
+        for (int t = 0; t < NTP; ++t) {
+          const uint64_t m = __ballot(k64[t] > T2);
+          selm[t] |= m;
+          need2 -= __popcll(m);
+        }
+        // ties at T2: ascending key index = slot-major, lane-minor
+        for (int t = 0; t < NTP; ++t) {
+          uint64_t tm = __ballot(k64[t] == T2);
+          while (need2 > 0 && tm) {
+            const uint64_t low = tm & (~tm + 1ull);
+            selm[t] |= low;
+            tm ^= low;
+            --need2;
+          }
+        }
+      }
+      // compact the chosen (index, score) pairs in ascending index order
+      int before = 0;
+#pragma unroll
+      for (int t = 0; t < NTP; ++t) {
+        const uint64_t mt = selm[t];
+        if ((mt >> l) & 1ull) {
+          const int pos = before + __popcll(mt & below);
+          const int j = l + 64 * t;
+          jl[w * NP + pos] = j;
+          S[i * NP + pos] = s[t];
+          if (idxg) idxg[(bh * n + qr) * (size_t)topk + pos] = j;
+        }
+        before += __popcll(mt);
+      }
+    }
+    __syncthreads();
+    if (row_ok) {
+      // ---- 3. gather ---------------------------------------------------------------
+      const int sg = l / 16;
+      const int dq = l % 16;
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+      for (int p = sg; p < topk; p += 4) {
+        const int j = jl[w * NP + p];
+        const double sj = S[i * NP + p];
+        const float4 vv = *reinterpret_cast<const float4 *>(vb + (size_t)j * DIM + 4 * dq);
+        acc[0] = fma(sj, (double)vv.x, acc[0]);
+        acc[1] = fma(sj, (double)vv.y, acc[1]);
+        acc[2] = fma(sj, (double)vv.z, acc[2]);
+        acc[3] = fma(sj, (double)vv.w, acc[3]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += __shfl_xor(acc[e], 16);
+        acc[e] += __shfl_xor(acc[e], 32);
+      }
+      if (sg == 0) {
+        const float4 o = {(float)acc[0], (float)acc[1], (float)acc[2], (float)acc[3]};
+        *reinterpret_cast<float4 *>(outg + (bh * n + qr) * DIM + 4 * dq) = o;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int NTP>
+hipError_t launch_ntp(const TopkArgs &a, hipStream_t stream) {
+  const size_t shmem = (size_t)64 * NTP * (QB * 8 + 4 * 4);
+  if (shmem > 65536) {  // opt in to more than 64 KiB of LDS (gfx950: 160 KiB)
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&topk_kernel<NTP>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((a.n + QB - 1) / QB, a.h, a.b);
+  topk_kernel<NTP><<<grid, kThreads, shmem, stream>>>(a.q, a.k, a.v, a.out,
+                                                      a.idx, a.h, a.n, a.topk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
+  const int nt = (a.n + 63) / 64;
+  if (nt <= 1) return launch_ntp<1>(a, stream);
+  if (nt <= 2) return launch_ntp<2>(a, stream);
+  if (nt <= 4) return launch_ntp<4>(a, stream);
+  if (nt <= 8) return launch_ntp<8>(a, stream);
+  return launch_ntp<16>(a, stream);
+}
+
+}  // namespace attn
