@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV-cache attention hot path on one MI355X.
+
+One step runs every operation of the path once over resident synthetic
+inputs, on the stream the library launches on:
+
+  decode   ragged batch: B=64, Hq=32, Hkv=8, D=128, bf16, static cache of
+           max_length 8192, per-sequence lengths uniform in [1, 8192]
+           (one attn_decode call for the whole batch)              <- headline
+  prefill  causal prefill: 16 heads, D=64, prefix 3072 + 1024 new tokens
+  topk     top-k sparse scores: b=32, 3 head groups, n=512, d=64, topk=64
+
+`value` is the decode KV-read bandwidth: algorithmic bytes (every valid K and
+V row once per kv head, plus q and out) divided by the decode time measured
+with HIP events around each decode call. Prefill TFLOP/s (causal FLOPs) and
+top-k figures are reported beside it. Inputs are synthetic (seeded N(0,1),
+bf16 rounded to nearest even), generated once and resident in HBM before the
+timed region starts.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+FP64_PEAK_TFLOPS = 78.6         # MI355X fp64 (vector and matrix)
+METRIC = ("decode KV-read GB/s (% HBM peak) at ctx 8192; "
+          "prefill TFLOP/s (% MFMA peak)")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate oracle time budget for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the single-sequence position-8000 figures")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# Inputs
+# ----------------------------------------------------------------------------
+def bf16_dev(arr, torch):
+    import numpy as np
+    t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def make_decode(torch, synth, tas):
+    import numpy as np
+    p = synth.WORKLOADS["decode_ragged_b64"].params
+    B, Hq, Hkv, D, M = p["B"], p["Hq"], p["Hkv"], p["D"], p["max_length"]
+    lens = synth.ragged_lengths(p["seed"], B, M)
+    q = torch.empty(B, Hq, D, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(B, Hkv, M, D, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    for b, L, qb, kb, vb in synth.iter_ragged(p["seed"], B, Hq, Hkv, D, M,
+                                               "bf16", lens):
+        q[b] = bf16_dev(qb, torch)
+        k[b, :, :L] = bf16_dev(kb, torch)
+        v[b, :, :L] = bf16_dev(vb, torch)
+    sl = torch.from_numpy(lens.astype(np.int32)).cuda()
+    out = torch.empty_like(q)
+    ws = torch.empty(max(1, tas.attn_decode_workspace_bytes(B, Hq, Hkv, D, M)),
+                     dtype=torch.uint8, device="cuda")
+    nbytes = 2 * Hkv * D * 2 * int(lens.sum()) + 2 * B * Hq * D * 2
+    return dict(p=p, q=q, k=k, v=v, seq_lens=sl, lens=lens, out=out, ws=ws,
+                bytes=nbytes)
+
+
+def make_prefill(torch, synth):
+    p = synth.WORKLOADS["prefill_prefix3072"].params
+    inp = synth.prefill(p["seed"], p["B"], p["Hq"], p["Hkv"], p["D"], p["Lq"],
+                        p["prefix_len"], p["max_length"], "bf16",
+                        poison=False, scale=p["scale"])
+    q, k, v = (bf16_dev(x, torch) for x in (inp.q, inp.k_cache, inp.v_cache))
+    D, H, Lq, P = p["D"], p["Hq"], p["Lq"], p["prefix_len"]
+    flops = 4 * D * H * p["B"] * sum(P + i + 1 for i in range(Lq))
+    return dict(p=p, q=q, k=k, v=v, out=torch.empty_like(q), flops=flops)
+
+
+def make_topk(torch, synth):
+    p = synth.WORKLOADS["topk_c2psa"].params
+    inp = synth.topk(p["seed"], p["b"], p["h"], p["n"], p["d"], p["topk"])
+    q, k, v = (torch.from_numpy(x).cuda() for x in (inp.q, inp.k, inp.v))
+    b, h, n, d, kk = p["b"], p["h"], p["n"], p["d"], p["topk"]
+    flops = b * h * (2 * n * n * d + 2 * n * kk * d)
+    return dict(p=p, q=q, k=k, v=v, out=torch.empty_like(q), flops=flops)
+
+
+# ----------------------------------------------------------------------------
+# Secondary: one sequence at position 8000 of an 8192-row cache
+# ----------------------------------------------------------------------------
+def bench_single_position(torch, tas, synth, copies=32, reps=20):
+    """Single-sequence GQA decode (B=1, Hq=32, Hkv=8, D=128, bf16) at
+    position 8000, replayed from a captured graph of `copies` calls. Cold:
+    each call reads a different cache copy (copies * 32 MiB, well past the
+    256 MiB MALL). Warm: every call reads the same copy."""
+    import numpy as np
+    p = synth.WORKLOADS["decode_gqa_static"].params
+    pos = 8000
+    inp = synth.decode_uniform(p["seed"], 1, p["Hq"], p["Hkv"], p["D"],
+                               p["max_length"], pos, "bf16", poison=False)
+    q = bf16_dev(inp.q, torch)
+    k0 = bf16_dev(inp.k_cache, torch)
+    v0 = bf16_dev(inp.v_cache, torch)
+    ks = [k0] + [k0.clone() for _ in range(copies - 1)]
+    vs = [v0] + [v0.clone() for _ in range(copies - 1)]
+    out = torch.empty_like(q)
+    ws = torch.empty(tas.attn_decode_workspace_bytes(1, 32, 8, 128, 8192),
+                     dtype=torch.uint8, device="cuda")
+    nbytes = 2 * 8 * 128 * 2 * (pos + 1) + 2 * 32 * 128 * 2
+    res = {}
+    s = torch.cuda.Stream()
+    for mode in ("cold", "warm"):
+        idx = list(range(copies)) if mode == "cold" else [0] * copies
+        with torch.cuda.stream(s):
+            for i in idx[:4]:  # warm-up outside capture
+                tas.attn_decode(q, ks[i], vs[i], position_id=pos,
+                                scale=p["scale"], out=out, workspace=ws)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in idx:
+                tas.attn_decode(q, ks[i], vs[i], position_id=pos,
+                                scale=p["scale"], out=out, workspace=ws)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):  # replay and events on the same stream
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+        res[mode] = dict(us_per_call=round(us, 3),
+                         GBps=round(nbytes / (us * 1e-6) / 1e9, 1))
+        del g
+    ref = out.float().cpu().numpy()
+    assert np.all(np.isfinite(ref))
+    del ks, vs
+    torch.cuda.empty_cache()
+    return dict(workload="decode_gqa_static_pos8000", bytes=nbytes,
+                calls_per_graph=copies, **res)
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the decode workload
+# ----------------------------------------------------------------------------
+def cpu_baseline(dec, synth, budget_s):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()]
+                      or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    p = dec["p"]
+    lens = dec["lens"]
+    done, nbytes, t_total = 0, 0, 0.0
+    gpu_out = dec["out"].float().cpu().numpy().astype(np.float64)
+    max_err = 0.0
+    for b in range(p["B"]):
+        L = int(lens[b])
+        qb, kb, vb = synth.ragged_sequence(p["seed"], b, p["Hq"], p["Hkv"],
+                                           p["D"], L, "bf16")
+        qf, kf, vf = (synth.bf16_to_f32(x) for x in (qb, kb, vb))
+        t0 = time.perf_counter()
+        ref = oracle.decode_sequence(qf, kf, vf, L, p["scale"])
+        t_total += time.perf_counter() - t0
+        max_err = max(max_err, float(np.max(np.abs(ref - gpu_out[b]))))
+        nbytes += 2 * p["Hkv"] * p["D"] * 2 * L + 2 * p["Hq"] * p["D"] * 2
+        done += 1
+        if t_total >= budget_s:
+            break
+    return dict(value=round(nbytes / t_total / 1e9, 4), unit="GB/s",
+                cores=int(threads), kind="oracle",
+                sample=(f"fp64 NumPy oracle over the first {done} of 64 "
+                        f"sequences of the ragged decode batch "
+                        f"({nbytes} algorithmic bytes in {t_total:.2f} s)"),
+                spot_check_max_abs_err=max_err)
+
+
+# ----------------------------------------------------------------------------
+# HBM traffic from committed counter summaries
+# ----------------------------------------------------------------------------
+def kernel_source_hash(name):
+    path = os.path.join(ROOT, "transformer_attention_split_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def committed_traffic(summary, source):
+    """Bytes per launch from a profiles/ summary, if it was taken on the
+    current kernel source (the summary records the source hash)."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("source_sha256_16") != kernel_source_hash(source):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): "
+            "the path has no multi-GPU component in this build.")
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    import transformer_attention_split_amd as tas
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    log("building inputs ...")
+    dec = make_decode(torch, synth, tas)
+    pre = make_prefill(torch, synth)
+    tk = make_topk(torch, synth)
+    torch.cuda.synchronize()
+    dp, pp = dec["p"], pre["p"]
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        log("calibration copy: 1 GiB device-to-device done")
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        tas.attn_decode(dec["q"], dec["k"], dec["v"], seq_lens=dec["seq_lens"],
+                        scale=dp["scale"], out=dec["out"], workspace=dec["ws"])
+        if ev:
+            ev[1].record()
+        tas.attn_prefill(pre["q"], pre["k"], pre["v"],
+                         prefix_len=pp["prefix_len"], scale=pp["scale"],
+                         out=pre["out"])
+        if ev:
+            ev[2].record()
+        tas.attn_topk(tk["q"], tk["k"], tk["v"], tk["p"]["topk"],
+                      out=tk["out"])
+        if ev:
+            ev[3].record()
+
+    log(f"warmup {args.warmup} steps ...")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for _ in range(args.steps)]
+    log(f"timing {args.steps} steps ...")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_dec = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3
+    t_pre = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
+    t_tk = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps * 1e-3
+    dec_gbps = dec["bytes"] / t_dec / 1e9
+    pre_tflops = pre["flops"] / t_pre / 1e12
+    tk_tflops = tk["flops"] / t_tk / 1e12
+    log(f"decode {t_dec * 1e6:.1f} us  {dec_gbps:.1f} GB/s | prefill "
+        f"{t_pre * 1e6:.1f} us {pre_tflops:.1f} TFLOP/s | topk "
+        f"{t_tk * 1e6:.1f} us {tk_tflops:.2f} TFLOP/s")
+
+    secondary = {
+        "prefill": dict(workload="prefill_prefix3072", us=round(t_pre * 1e6, 2),
+                        TFLOPs=round(pre_tflops, 2),
+                        frac_of_bf16_mfma_peak=round(
+                            pre_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                        flops=pre["flops"]),
+        "topk": dict(workload="topk_c2psa", us=round(t_tk * 1e6, 2),
+                     TFLOPs=round(tk_tflops, 3),
+                     frac_of_fp64_peak=round(tk_tflops / FP64_PEAK_TFLOPS, 4),
+                     flops=tk["flops"]),
+    }
+    if not args.no_secondary:
+        log("single-sequence position-8000 decode (graph replay) ...")
+        secondary["decode_single_pos8000"] = bench_single_position(
+            torch, tas, synth)
+
+    traffic = committed_traffic("decode_split_kernel_traffic.txt",
+                                "decode.hip")
+    roofline = {
+        "kernel": "decode_split_kernel+decode_combine_kernel (one attn_decode call)",
+        "bound": "hbm", "achieved": round(dec_gbps, 1),
+        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": dec["bytes"],
+        "avg_launch_us": round(t_dec * 1e6, 2),
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(dec, synth, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(dec_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_ragged_b64",
+            "B": dp["B"], "Hq": dp["Hq"], "Hkv": dp["Hkv"], "D": dp["D"],
+            "max_length": dp["max_length"],
+            "sum_valid_rows": int(dec["lens"].sum()),
+            "step_also_runs": ["prefill_prefix3072", "topk_c2psa"],
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
