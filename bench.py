@@ -81,7 +81,7 @@ def make_decode(torch, synth, tas):
         v[b, :, :L] = bf16_dev(vb, torch)
     sl = torch.from_numpy(lens.astype(np.int32)).cuda()
     out = torch.empty_like(q)
-    ws = torch.empty(max(1, tas.attn_decode_workspace_bytes(B, Hq, Hkv, D, M)),
+    ws = torch.zeros(max(1, tas.attn_decode_workspace_bytes(B, Hq, Hkv, D, M)),
                      dtype=torch.uint8, device="cuda")
     nbytes = 2 * Hkv * D * 2 * int(lens.sum()) + 2 * B * Hq * D * 2
     return dict(p=p, q=q, k=k, v=v, seq_lens=sl, lens=lens, out=out, ws=ws,
@@ -127,7 +127,7 @@ def bench_single_position(torch, tas, synth, copies=32, reps=20):
     ks = [k0] + [k0.clone() for _ in range(copies - 1)]
     vs = [v0] + [v0.clone() for _ in range(copies - 1)]
     out = torch.empty_like(q)
-    ws = torch.empty(tas.attn_decode_workspace_bytes(1, 32, 8, 128, 8192),
+    ws = torch.zeros(tas.attn_decode_workspace_bytes(1, 32, 8, 128, 8192),
                      dtype=torch.uint8, device="cuda")
     nbytes = 2 * 8 * 128 * 2 * (pos + 1) + 2 * 32 * 128 * 2
     res = {}

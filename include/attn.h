@@ -106,12 +106,14 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D,
  *   scale      multiplier of q·k; any finite value (the Python binding
  *              passes 1/sqrt(D) when the caller gives none).
  *   split_rows cache rows per split-KV work item (0 = automatic). Forcing it
- *              changes only the reduction order, never the math.
+ *              changes only the reduction order, never the math. At most
+ *              1024 splits per sequence: a smaller value is raised to
+ *              ceil(max_length / 1024).
  *   workspace  device scratch of at least
  *              attn_decode_workspace_bytes(B,Hq,Hkv,D,max_length,split_rows)
- *              bytes, 256-byte aligned; no initial contents required. Its
- *              contents are undefined after the call. Concurrent calls need
- *              distinct workspaces.
+ *              bytes, 256-byte aligned, for the per-split partial results; no
+ *              initial contents required, contents undefined after the call.
+ *              Calls that may overlap need distinct workspaces.
  * Supported: D in {64, 128}; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8};
  * B, Hkv <= 65535. B == 0 is a no-op. */
 int attn_decode(int dtype, const void *q, const void *k_cache,

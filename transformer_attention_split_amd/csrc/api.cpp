@@ -47,36 +47,43 @@ bool fits(std::initializer_list<double> dims) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode planning. A work item is (split, kv head, sequence). The automatic
-// choice aims for about kTargetBlocks workgroups so every CU has several to
-// interleave, with at least kMinSplitRows rows per split so a workgroup's
-// 16-byte-per-lane loads stay deep enough to cover HBM latency.
+// Decode planning. A work item is (kv head, sequence, split). The automatic
+// choice aims for about kTargetBlocks workgroups (about half of them hold no
+// rows for uniformly ragged lengths and exit at once) with a split length
+// that is a whole number of rounds of the workgroup's four wave tiles (one
+// wave tile is 8 KiB of K: 4096/D rows). At most attn::kDecodeMaxSplits
+// splits per sequence: a smaller forced split_rows is raised to
+// ceil(max_length / kDecodeMaxSplits).
 // ---------------------------------------------------------------------------
-constexpr long kTargetBlocks = 8192;
-constexpr int kMaxSplits = 1024;
-constexpr int kMinSplitRows = 128;
-constexpr int kRowQuantum = 64;
+constexpr long kTargetBlocks = 4096;
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+int row_quantum(int D) { return 4 * (4096 / D); }
+
+int effective_split_rows(int max_length, int split_rows) {
+  const int floor_rows = ceil_div(max_length, attn::kDecodeMaxSplits);
+  return split_rows < floor_rows ? floor_rows : split_rows;
+}
 
 int auto_split_target(int B, int Hkv) {
   long items = (long)B * Hkv;
   long s = (kTargetBlocks + items - 1) / items;
   if (s < 1) s = 1;
-  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > attn::kDecodeMaxSplits) s = attn::kDecodeMaxSplits;
   return (int)s;
 }
 
-attn::DecodePlan plan_decode(int B, int Hkv, int L_bound, int split_rows) {
+attn::DecodePlan plan_decode(int B, int Hkv, int D, int max_length,
+                             int L_bound, int split_rows) {
   attn::DecodePlan p{};
   if (split_rows > 0) {
-    p.split_rows = split_rows;
+    p.split_rows = effective_split_rows(max_length, split_rows);
   } else {
-    const int target = auto_split_target(B, Hkv);
-    int sr = ceil_div(L_bound, target);
-    sr = ceil_div(sr, kRowQuantum) * kRowQuantum;
-    if (sr < kMinSplitRows) sr = kMinSplitRows;
-    p.split_rows = sr;
+    const int q = row_quantum(D);
+    int sr = ceil_div(L_bound, auto_split_target(B, Hkv));
+    sr = ceil_div(sr, q) * q;
+    p.split_rows = effective_split_rows(max_length, sr);
   }
   p.splits = ceil_div(L_bound, p.split_rows);
   if (p.splits < 1) p.splits = 1;
@@ -84,10 +91,11 @@ attn::DecodePlan plan_decode(int B, int Hkv, int L_bound, int split_rows) {
 }
 
 // Upper bound on splits for any valid length <= max_length.
-int max_splits(int B, int Hkv, int max_length, int split_rows) {
-  if (split_rows > 0) return ceil_div(max_length, split_rows);
+int max_splits(int B, int Hkv, int D, int max_length, int split_rows) {
+  if (split_rows > 0)
+    return ceil_div(max_length, effective_split_rows(max_length, split_rows));
   int a = auto_split_target(B, Hkv);
-  int b = ceil_div(max_length, kMinSplitRows);
+  int b = ceil_div(max_length, row_quantum(D));
   return a < b ? a : b;
 }
 
@@ -126,7 +134,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D,
   if (B == 0) return 0;
   if (!fits({(double)B, (double)Hq, (double)max_length, (double)D}))
     return 0;
-  const int S = max_splits(B, Hkv, max_length, split_rows);
+  const int S = max_splits(B, Hkv, D, max_length, split_rows);
   return ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S, D);
 }
 
@@ -192,10 +200,11 @@ int attn_decode(int dtype, const void *q, const void *k_cache,
   a.position_id = position_id;
   a.seq_lens = seq_lens;
   a.scale = scale;
-  a.plan = plan_decode(B, Hkv, L_bound, split_rows);
-  a.ws_ml = static_cast<float *>(workspace);
-  a.ws_o = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                     ws_ml_bytes(B, Hq, a.plan.splits));
+  a.plan = plan_decode(B, Hkv, D, max_length, L_bound, split_rows);
+  char *ws = static_cast<char *>(workspace);
+  a.ws_ml = reinterpret_cast<float *>(ws);
+  ws += ws_ml_bytes(B, Hq, a.plan.splits);
+  a.ws_o = reinterpret_cast<float *>(ws);
   hipError_t e = attn::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attn_decode launch");
   return ok();

@@ -2,94 +2,400 @@
 //
 // Operation: "MiniCPM4 forward_step Attention Performance Fix", §3 and §4.1 —
 // the query of the new token attends only to cache rows [0, position_id]
-// (or [0, seq_len) per sequence), and the slice bound replaces the mask, so
-// work and bytes read are proportional to the valid length (§2.4 cost table).
+// (or [0, seq_len) per sequence); the slice bound replaces the mask, so the
+// work and the bytes read are proportional to the valid length (§2.4 cost
+// table). Query head h reads kv head h / G (G = Hq/Hkv), so each K and V row
+// is read once and serves the whole group of G query heads.
 //
-// Two kernels:
-//   decode_split_kernel   grid (split, kv head, batch). One workgroup streams
-//       the K and V rows of its split once and serves every query head of the
-//       kv group from that single read. Each cache row is read by a group of
-//       LPR lanes with one 16-byte load per lane (a wave covers 64/LPR
-//       consecutive rows, 1 KiB contiguous); the per-row dot products are
-//       reduced with DPP row operations; softmax is the online (running max /
-//       running sum) form in the exp2 domain with scale*log2(e) folded into q.
-//       The workgroup merges its row groups and writes one partial
-//       (max, sum, unnormalised output) per query head.
-//   decode_combine_kernel grid (query head, batch). Log-sum-exp merge of the
-//       partials of the splits that hold rows, division by the total sum and
-//       the cast to the output type.
+// Work item = (kv head g, sequence b, split s) = cache rows
+// [s*split_rows, min((s+1)*split_rows, L_b)). The grid is (Hkv, B, splits):
+// the split index varies slowest, so the round-robin dispatch over the 8 XCDs
+// spreads every split index evenly over them (a split-fastest order would
+// pin split s to XCD s % 8 and, with ragged lengths, load the low XCDs far
+// more than the high ones), and splits that hold no rows are dispatched last
+// and exit at once.
+//
+// bf16 (decode_bf16_kernel): each of the 4 waves walks its own tiles of BN
+// rows (BN*D*2 = 8 KiB of K and of V per tile) with non-temporal 16-byte
+// loads, and runs both products on the bf16 matrix cores — the kernel stays
+// bound by HBM; the matrix cores only take the multiply-adds off the vector
+// ALUs, which would otherwise need more issue slots per byte than a CU has:
+//   Sᵀ = K·Qᵀ  v_mfma_f32_16x16x32_bf16, A = 16 K rows straight from the
+//              loads, B = the G query heads of the group (columns >= G zero);
+//              lane (q, lane-group) receives 4 keys of query q;
+//   softmax    online, exp2 domain (scale*log2 e applied to fp32 scores); the
+//              running max is reduced over the 4 lanes that share a query;
+//              the output is rescaled only when some running max moved;
+//   Oᵀ += Vᵀ·Pᵀ  V rows are transposed through this wave's LDS tile (eight
+//              rows per lane packed into 16-byte writes), P is rounded to
+//              bf16 and stays in registers.
+// fp32 (decode_f32_kernel): vector-ALU form — each cache row is read by a
+// group of D/4 lanes (16-byte loads), dot products reduced with DPP row
+// operations, online softmax per group.
+//
+// Both end the same way: the workgroup merges its waves / row groups and
+// either writes the output directly (the sequence has a single split) or
+// writes one partial (running max, running sum, unnormalised output) per
+// query head to the workspace. decode_combine_kernel then merges the
+// partials of every multi-split sequence in split order (log-sum-exp),
+// divides by the total sum and casts to the output type. (Merging inside the
+// split kernel, in the last workgroup to finish, needs device-scope fences
+// per workgroup and a serial merge; both measured far slower than the
+// second launch.)
 #include "common.h"
 #include "launch.h"
 
 namespace attn {
 namespace {
 
-template <bool BF16, int VEC>
-__device__ __forceinline__ void unpack(const uint4 &w, float (&f)[VEC]) {
-  if constexpr (BF16) {
-    static_assert(VEC == 8, "bf16 chunk holds 8 values");
-    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16lo(x[i]);
-      f[2 * i + 1] = bf16hi(x[i]);
-    }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4_t ldnt(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+struct Item {
+  int L;        // valid rows of the sequence
+  int row0;     // first row of this split
+  int row1;     // one past the last row of this split
+  int n_split;  // splits of this sequence that hold rows
+};
+
+__device__ __forceinline__ Item make_item(const int32_t *seq_lens, int b,
+                                          int position_id, int max_length,
+                                          int split_rows, int s) {
+  Item it;
+  if (seq_lens == nullptr) {
+    it.L = position_id + 1;
   } else {
-    static_assert(VEC == 4, "f32 chunk holds 4 values");
-    f[0] = __uint_as_float(w.x);
-    f[1] = __uint_as_float(w.y);
-    f[2] = __uint_as_float(w.z);
-    f[3] = __uint_as_float(w.w);
+    int L = seq_lens[b];
+    it.L = L < 0 ? 0 : (L > max_length ? max_length : L);
+  }
+  it.row0 = s * split_rows;
+  it.row1 = min(it.row0 + split_rows, it.L);
+  it.n_split = (it.L + split_rows - 1) / split_rows;
+  return it;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out(void *outp, size_t idx, float x) {
+  if constexpr (BF16) {
+    static_cast<uint16_t *>(outp)[idx] = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+  } else {
+    static_cast<float *>(outp)[idx] = x;
   }
 }
 
-__device__ __forceinline__ int valid_length(const int32_t *seq_lens, int b,
-                                            int position_id, int max_length) {
-  if (seq_lens == nullptr) return position_id + 1;
-  int L = seq_lens[b];
-  return L < 0 ? 0 : (L > max_length ? max_length : L);
+// Shared ending. fin_m/fin_l/fin_o (LDS) hold this workgroup's merged
+// running max, sum and unnormalised output of the G query heads of (b, g).
+// A sequence with a single split is finished here; otherwise the partial is
+// written for the combine kernel.
+template <bool BF16, int D, int G, int NT>
+__device__ __forceinline__ void finish(const float *fin_m, const float *fin_l,
+                                       const float *fin_o, const Item &it,
+                                       int b, int g, int s, int Hq,
+                                       int splits, void *outp, float *ws_ml,
+                                       float *ws_o) {
+  const int tid = threadIdx.x;
+  const size_t head0 = (size_t)b * Hq + (size_t)g * G;
+  if (it.n_split == 1) {
+    for (int i = tid; i < G * D; i += NT) {
+      const int h = i / D, d = i % D;
+      store_out<BF16>(outp, (head0 + h) * D + d, fin_o[h * D + d] / fin_l[h]);
+    }
+    return;
+  }
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D, d = i % D;
+    ws_o[((head0 + h) * splits + s) * D + d] = fin_o[h * D + d];
+  }
+  if (tid < G) {
+    float *ml = ws_ml + ((head0 + tid) * splits + s) * 2;
+    ml[0] = fin_m[tid];
+    ml[1] = fin_l[tid];
+  }
 }
 
-template <bool BF16, int D, int G, int U>
-__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
-    const void *__restrict__ qp, const void *__restrict__ kp,
-    const void *__restrict__ vp, const int32_t *__restrict__ seq_lens,
-    int position_id, float *__restrict__ ws_ml, float *__restrict__ ws_o,
-    int Hq, int Hkv, int max_length, int split_rows, int splits,
-    float qscale) {
-  constexpr int ELT = BF16 ? 2 : 4;
-  constexpr int VEC = 16 / ELT;             // values per 16-byte chunk
-  constexpr int LPR = D / VEC;              // lanes per cache row
-  constexpr int NG = kDecodeThreads / LPR;  // row groups per workgroup
-  constexpr int NW = kDecodeThreads / 64;   // waves per workgroup
-  static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "row layout");
+template <bool BF16, int D, int G, int NT>
+__device__ __forceinline__ void write_zero_rows(void *outp, int b, int g,
+                                                int Hq) {
+  const size_t head0 = (size_t)b * Hq + (size_t)g * G;
+  for (int i = threadIdx.x; i < G * D; i += NT) store_out<BF16>(outp, head0 * D + i, 0.f);
+}
 
-  const int s = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int L = valid_length(seq_lens, b, position_id, max_length);
-  const int row0 = s * split_rows;
-  if (row0 >= L) return;  // uniform over the workgroup
-  const int row1 = min(row0 + split_rows, L);
+// ---------------------------------------------------------------------------
+// bf16: matrix-core form
+// ---------------------------------------------------------------------------
+constexpr int kThreads = kDecodeThreads;  // 4 waves
 
+template <int D>
+struct Bf16Tile {
+  static constexpr int BN = 4096 / D;      // rows per wave tile (8 KiB of K)
+  static constexpr int KS = D / 32;        // k-steps of K·Qᵀ
+  static constexpr int NDB = D / 16;       // 16-wide output blocks
+  static constexpr int NKB = BN / 16;      // 16-row blocks per tile
+  static constexpr int SV = BN + 4;        // Vᵀ row stride in LDS (elements)
+  static constexpr int NOCT = BN / 8;      // 8-row groups per tile
+  static constexpr int VT_BYTES = D * SV * 2;
+  static_assert(NOCT * (D / 8) == 64, "one V transpose item per lane");
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
+    const uint16_t *__restrict__ qg, const uint16_t *__restrict__ kg,
+    const uint16_t *__restrict__ vg, const int32_t *__restrict__ seq_lens,
+    int position_id, void *__restrict__ outp, float *__restrict__ ws_ml,
+    float *__restrict__ ws_o, int Hq, int Hkv,
+    int max_length, int split_rows, int splits, float qk_scale) {
+  using T = Bf16Tile<D>;
+  constexpr int BN = T::BN, KS = T::KS, NDB = T::NDB, NKB = T::NKB;
+  constexpr int SV = T::SV;
+  constexpr int LDS_MAIN = 4 * T::VT_BYTES;
+  constexpr int LDS_FIN = (4 * G * D + 8 * 16) * 4;
+  constexpr int LDS_BYTES = LDS_MAIN > LDS_FIN ? LDS_MAIN : LDS_FIN;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
+  __shared__ float fin_m[G], fin_l[G];
+
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int s = blockIdx.z;
+  const Item it = make_item(seq_lens, b, position_id, max_length, split_rows, s);
+  if (it.row0 >= it.L) {
+    if (it.L == 0 && s == 0) write_zero_rows<true, D, G, kThreads>(outp, b, g, Hq);
+    return;
+  }
   const int tid = threadIdx.x;
-  const int lr = tid % LPR;   // lane inside the row group
-  const int grp = tid / LPR;  // row group
+  const int w = tid / 64;
+  const int l = tid % 64;
+  const int li = l % 16;   // query column / row within a 16-row block
+  const int lg = l / 16;   // lane group (k slots 8*lg..8*lg+7)
 
-  // Query heads g*G .. g*G+G-1, this lane's VEC dimensions, prescaled.
-  float qv[G][VEC];
+  // Query heads of the group as the B operand of Sᵀ = K·Qᵀ (column li).
+  bf16x8_t qf[KS];
   {
-    const char *qb = static_cast<const char *>(qp) +
-                     (((size_t)b * Hq + (size_t)g * G) * D + lr * VEC) * ELT;
+    const uint16_t *qrow = qg + ((size_t)b * Hq + (size_t)g * G + li) * D;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(qb + (size_t)h * D * ELT);
-      unpack<BF16, VEC>(w, qv[h]);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) qv[h][e] *= qscale;
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (li < G) v = *reinterpret_cast<const u32x4_t *>(qrow + ks * 32 + 8 * lg);
+      qf[ks] = as_bf16x8(v);
     }
   }
 
+  const size_t kvbase = ((size_t)b * Hkv + g) * (size_t)max_length * D;
+  const uint16_t *kb = kg + kvbase;
+  const uint16_t *vb = vg + kvbase;
+  uint16_t *vt = reinterpret_cast<uint16_t *>(smem + w * T::VT_BYTES);
+  const int oct = l % T::NOCT;  // V transpose item: rows 8*oct..8*oct+7
+  const int ch = l / T::NOCT;   //                   dims 8*ch..8*ch+7
+
+  f32x4_t o[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kNegInf;
+  float lsum = 0.f;
+
+  for (int t0 = it.row0 + w * BN; t0 < it.row1; t0 += 4 * BN) {
+    const bool full = t0 + BN <= it.row1;
+    // ---- loads: K in the A-operand layout, V as 8-row groups ----------------
+    u32x4_t kf[NKB][KS];
+#pragma unroll
+    for (int kb16 = 0; kb16 < NKB; ++kb16) {
+      const int row = t0 + kb16 * 16 + li;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (full || row < it.row1) v = ldnt(kb + (size_t)row * D + ks * 32 + 8 * lg);
+        kf[kb16][ks] = v;
+      }
+    }
+    u32x4_t vr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = t0 + 8 * oct + i;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (full || row < it.row1) v = ldnt(vb + (size_t)row * D + 8 * ch);
+      vr[i] = v;
+    }
+    // ---- Sᵀ = K·Qᵀ --------------------------------------------------------------
+    f32x4_t sc[NKB];
+#pragma unroll
+    for (int kb16 = 0; kb16 < NKB; ++kb16) {
+      sc[kb16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sc[kb16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(kf[kb16][ks]), qf[ks], sc[kb16], 0, 0, 0);
+    }
+    // ---- V rows -> Vᵀ in LDS (keys 8*oct..8*oct+7 of dims 8*ch..8*ch+7) ----
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int wi = e / 2;
+      u32x4_t pk;
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const uint32_t a = vr[2 * pr][wi], c = vr[2 * pr + 1][wi];
+        pk[pr] = (e & 1) ? ((a >> 16) | (c & 0xffff0000u))
+                         : ((a & 0xffffu) | (c << 16));
+      }
+      // rows of Vᵀ are 8-byte aligned (stride SV): two 8-byte writes
+      u32x2_t *dst = reinterpret_cast<u32x2_t *>(&vt[(8 * ch + e) * SV + 8 * oct]);
+      dst[0] = u32x2_t{pk[0], pk[1]};
+      dst[1] = u32x2_t{pk[2], pk[3]};
+    }
+    // ---- online softmax -----------------------------------------------------------
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb16 = 0; kb16 < NKB; ++kb16) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = sc[kb16][r] * qk_scale;
+        if (!full && t0 + kb16 * 16 + 4 * lg + r >= it.row1) x = kNegInf;
+        sc[kb16][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);  // finite: the tile's first row is valid
+    if (__any(mnew > m)) {
+      const float alpha = fast_exp2(m - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      m = mnew;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- Oᵀ += Vᵀ·Pᵀ ---------------------------------------------------------------
+#pragma unroll
+    for (int t2 = 0; t2 < BN / 32; ++t2) {
+      float p[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = fast_exp2(sc[2 * t2][r] - m);
+        p[4 + r] = fast_exp2(sc[2 * t2 + 1][r] - m);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lsum += p[e];
+      const u32x4_t pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+      const bf16x8_t pb = as_bf16x8(pw);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint16_t *vrow = &vt[(db * 16 + li) * SV + 32 * t2 + 4 * lg];
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 16);
+        const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), pb,
+                                                       o[db], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- merge the 4 waves -----------------------------------------------------------
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  __syncthreads();  // every wave is done with its Vᵀ tile
+  float *wm = reinterpret_cast<float *>(smem);  // [4][16]
+  float *wl = wm + 4 * 16;                      // [4][16]
+  float *wo = wl + 4 * 16;                      // [4][G][D]
+  if (lg == 0) {
+    wm[w * 16 + li] = m;
+    wl[w * 16 + li] = lsum;
+  }
+  if (li < G) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4_t *>(&wo[(w * G + li) * D + db * 16 + 4 * lg]) = o[db];
+  }
+  __syncthreads();
+  float *fo = wo;  // merged output overwrites wave 0's slot, read first
+  if (tid < G) {
+    float x = wm[tid];
+    for (int i = 1; i < 4; ++i) x = fmaxf(x, wm[i * 16 + tid]);
+    float lt = 0.f;
+    for (int i = 0; i < 4; ++i) lt += fast_exp2(wm[i * 16 + tid] - x) * wl[i * 16 + tid];
+    fin_m[tid] = x;
+    fin_l[tid] = lt;
+  }
+  __syncthreads();
+  float acc[(G * D + kThreads - 1) / kThreads];
+#pragma unroll
+  for (int j = 0; j * kThreads < G * D; ++j) {
+    const int i = tid + j * kThreads;
+    acc[j] = 0.f;
+    if (i < G * D) {
+      const int h = i / D;
+      const float mh = fin_m[h];
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww)
+        acc[j] = fmaf(fast_exp2(wm[ww * 16 + h] - mh), wo[ww * G * D + i], acc[j]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j * kThreads < G * D; ++j) {
+    const int i = tid + j * kThreads;
+    if (i < G * D) fo[i] = acc[j];
+  }
+  __syncthreads();
+  finish<true, D, G, kThreads>(fin_m, fin_l, fo, it, b, g, s, Hq, splits,
+                               outp, ws_ml, ws_o);
+}
+
+// ---------------------------------------------------------------------------
+// fp32: vector-ALU form
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void decode_f32_kernel(
+    const float *__restrict__ qp, const float *__restrict__ kp,
+    const float *__restrict__ vp, const int32_t *__restrict__ seq_lens,
+    int position_id, void *__restrict__ outp, float *__restrict__ ws_ml,
+    float *__restrict__ ws_o, int Hq, int Hkv,
+    int max_length, int split_rows, int splits, float qscale) {
+  constexpr int VEC = 4;                // floats per 16-byte chunk
+  constexpr int LPR = D / VEC;          // lanes per cache row (16 or 32)
+  constexpr int NG = kThreads / LPR;    // row groups per workgroup
+  constexpr int U = 4;                  // rows per group per iteration
+  __shared__ float sm_m[NG][G];
+  __shared__ float sm_l[NG][G];
+  __shared__ float sm_o[G * D];
+  __shared__ float fin_m[G], fin_l[G];
+
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int s = blockIdx.z;
+  const Item it = make_item(seq_lens, b, position_id, max_length, split_rows, s);
+  if (it.row0 >= it.L) {
+    if (it.L == 0 && s == 0) write_zero_rows<false, D, G, kThreads>(outp, b, g, Hq);
+    return;
+  }
+  const int tid = threadIdx.x;
+  const int lr = tid % LPR;
+  const int grp = tid / LPR;
+
+  float qv[G][VEC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float4 x = *reinterpret_cast<const float4 *>(
+        qp + ((size_t)b * Hq + (size_t)g * G + h) * D + lr * VEC);
+    qv[h][0] = x.x * qscale;
+    qv[h][1] = x.y * qscale;
+    qv[h][2] = x.z * qscale;
+    qv[h][3] = x.w * qscale;
+  }
   float m[G], l[G], o[G][VEC];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -98,53 +404,43 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
 #pragma unroll
     for (int e = 0; e < VEC; ++e) o[h][e] = 0.f;
   }
-
   const size_t rowbase = ((size_t)b * Hkv + g) * (size_t)max_length;
-  constexpr size_t RB = (size_t)D * ELT;  // bytes per cache row
-  const char *kb = static_cast<const char *>(kp) + rowbase * RB + lr * 16;
-  const char *vb = static_cast<const char *>(vp) + rowbase * RB + lr * 16;
+  const float *kb = kp + rowbase * D + lr * VEC;
+  const float *vb = vp + rowbase * D + lr * VEC;
 
-  for (int r = row0 + grp; r < row1; r += NG * U) {
-    uint4 kr[U], vr[U];
+  for (int r = it.row0 + grp; r < it.row1; r += NG * U) {
+    u32x4_t kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int rr = r + u * NG;
-      if (rr < row1) {
-        kr[u] = *reinterpret_cast<const uint4 *>(kb + (size_t)rr * RB);
-        vr[u] = *reinterpret_cast<const uint4 *>(vb + (size_t)rr * RB);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = make_uint4(0, 0, 0, 0);
+      kr[u] = u32x4_t{0u, 0u, 0u, 0u};
+      vr[u] = kr[u];
+      if (rr < it.row1) {
+        kr[u] = ldnt(kb + (size_t)rr * D);
+        vr[u] = ldnt(vb + (size_t)rr * D);
       }
     }
-    // Scores (already in the log2 domain through qscale).
     float sc[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float kf[VEC];
-      unpack<BF16, VEC>(kr[u], kf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc = fmaf(qv[h][e], kf[e], acc);
+        for (int e = 0; e < VEC; ++e) acc = fmaf(qv[h][e], __uint_as_float(kr[u][e]), acc);
         sc[u][h] = group_sum<LPR>(acc);
       }
-      if (r + u * NG >= row1) {
+      if (r + u * NG >= it.row1) {
 #pragma unroll
         for (int h = 0; h < G; ++h) sc[u][h] = kNegInf;
       }
     }
-    float vf[U][VEC];
-#pragma unroll
-    for (int u = 0; u < U; ++u) unpack<BF16, VEC>(vr[u], vf[u]);
-    // Online softmax update, once per U rows.
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mx = sc[0][h];
 #pragma unroll
       for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][h]);
-      const float mnew = fmaxf(m[h], mx);  // finite: row r is valid
+      const float mnew = fmaxf(m[h], mx);
       const float alpha = fast_exp2(m[h] - mnew);
       float p[U];
       float ps = 0.f;
@@ -158,130 +454,132 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(
       for (int e = 0; e < VEC; ++e) {
         float acc = o[h][e] * alpha;
 #pragma unroll
-        for (int u = 0; u < U; ++u) acc = fmaf(p[u], vf[u][e], acc);
+        for (int u = 0; u < U; ++u) acc = fmaf(p[u], __uint_as_float(vr[u][e]), acc);
         o[h][e] = acc;
       }
       m[h] = mnew;
     }
   }
 
-  // ---- merge the row groups of the workgroup --------------------------------
-  __shared__ float sm_m[NG][G];
-  __shared__ float sm_l[NW][G];
-  __shared__ float sm_o[NW][G][D];
+  // merge the row groups: common max, rescale, sum (fixed order)
   if (lr == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) sm_m[grp][h] = m[h];
-  }
-  __syncthreads();
-  float M[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x = sm_m[0][h];
-    for (int i = 1; i < NG; ++i) x = fmaxf(x, sm_m[i][h]);
-    M[h] = x;  // finite: at least one group holds a row
-    const float w = fast_exp2(m[h] - M[h]);  // 0 for an empty group
-    l[h] *= w;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) o[h][e] *= w;
-  }
-  // Sum over the row groups of a wave (lanes with equal lr).
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
     for (int h = 0; h < G; ++h) {
-      l[h] += __shfl_xor(l[h], off);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) o[h][e] += __shfl_xor(o[h][e], off);
-    }
-  }
-  const int wave = tid / 64;
-  const int lane = tid % 64;
-  if (lane < LPR) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) sm_o[wave][h][lr * VEC + e] = o[h][e];
-      if (lr == 0) sm_l[wave][h] = l[h];
+      sm_m[grp][h] = m[h];
+      sm_l[grp][h] = l[h];
     }
   }
   __syncthreads();
-  const size_t head0 = (size_t)b * Hq + (size_t)g * G;
-  for (int i = tid; i < G * D; i += kDecodeThreads) {
-    const int h = i / D, d = i % D;
-    float x = sm_o[0][h][d];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) x += sm_o[w][h][d];
-    ws_o[((head0 + h) * splits + s) * D + d] = x;
-  }
   if (tid < G) {
-    float x = sm_l[0][tid];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) x += sm_l[w][tid];
-    float *ml = ws_ml + ((head0 + tid) * splits + s) * 2;
-    ml[0] = M[tid];
-    ml[1] = x;
+    float x = sm_m[0][tid];
+    for (int i = 1; i < NG; ++i) x = fmaxf(x, sm_m[i][tid]);
+    float lt = 0.f;
+    for (int i = 0; i < NG; ++i) lt += fast_exp2(sm_m[i][tid] - x) * sm_l[i][tid];
+    fin_m[tid] = x;
+    fin_l[tid] = lt;
   }
+  for (int i = tid; i < G * D; i += kThreads) sm_o[i] = 0.f;
+  __syncthreads();
+  float w[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) w[h] = fast_exp2(m[h] - fin_m[h]);
+  // groups add their rescaled output one at a time (deterministic order)
+  for (int i = 0; i < NG; ++i) {
+    if (grp == i) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sm_o[h * D + lr * VEC + e] += w[h] * o[h][e];
+    }
+    __syncthreads();
+  }
+  finish<false, D, G, kThreads>(fin_m, fin_l, sm_o, it, b, g, s, Hq, splits,
+                                outp, ws_ml, ws_o);
 }
 
-template <bool BF16, int D>
-__global__ __launch_bounds__(64) void decode_combine_kernel(
+// ---------------------------------------------------------------------------
+// Combine: one workgroup per (kv head, sequence) with more than one split;
+// wave h merges query head g*G+h. Lane t takes the (max, sum) of splits
+// t, t+64, ...; the wave reduces the global max, the weights 2^(m_s - M)
+// go to LDS, and every lane then sums its output dimensions over the splits
+// in split order with independent (unrolled) loads.
+// ---------------------------------------------------------------------------
+
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(64 * G) void decode_combine_kernel(
     const float *__restrict__ ws_ml, const float *__restrict__ ws_o,
     const int32_t *__restrict__ seq_lens, int position_id,
     void *__restrict__ outp, int Hq, int max_length, int split_rows,
     int splits) {
-  constexpr int PER = D / 64;  // output values per lane
-  const int h = blockIdx.x;
+  constexpr int PER = D / 64;  // output dimensions per lane
+  __shared__ float wsh[G][kDecodeMaxSplits];
+  const int g = blockIdx.x;
   const int b = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int L = valid_length(seq_lens, b, position_id, max_length);
-  const int n = (L + split_rows - 1) / split_rows;  // splits holding rows
-  const size_t head = (size_t)b * Hq + h;
+  const Item it = make_item(seq_lens, b, position_id, max_length, split_rows, 0);
+  const int n = it.n_split;
+  if (n <= 1) return;  // finished by the split kernel (or zero rows)
+  const int h = threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  const size_t head = (size_t)b * Hq + (size_t)g * G + h;
+  const float *ml = ws_ml + head * splits * 2;
+  float mx = kNegInf;
+  for (int t = lane; t < n; t += 64) mx = fmaxf(mx, ml[2 * t]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float lt = 0.f;
+  for (int t = lane; t < n; t += 64) {
+    const float w = fast_exp2(ml[2 * t] - mx);
+    wsh[h][t] = w;
+    lt = fmaf(w, ml[2 * t + 1], lt);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lt += __shfl_xor(lt, off);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float *o = ws_o + head * splits * D + lane * PER;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float lsum = 1.f;
-  if (n > 0) {
-    const float *ml = ws_ml + head * splits * 2;
-    const float *o = ws_o + head * splits * D + lane * PER;
-    float M = ml[0];
-    for (int s = 1; s < n; ++s) M = fmaxf(M, ml[2 * s]);
-    lsum = 0.f;
-    for (int s = 0; s < n; ++s) {
-      const float w = fast_exp2(ml[2 * s] - M);
-      lsum = fmaf(w, ml[2 * s + 1], lsum);
+  int t = 0;
+  for (; t + 8 <= n; t += 8) {
+    float v[8][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[(size_t)s * D + e], acc[e]);
-    }
-  }
-  if constexpr (BF16) {
-    uint16_t *out = static_cast<uint16_t *>(outp) + head * D + lane * PER;
-    if constexpr (PER == 2) {
-      *reinterpret_cast<uint32_t *>(out) =
-          pack_bf16x2(acc[0] / lsum, acc[1] / lsum);
-    } else {
-      const uint32_t w = pack_bf16x2(acc[0] / lsum, 0.f);
-      out[0] = (uint16_t)(w & 0xffffu);
-    }
-  } else {
-    float *out = static_cast<float *>(outp) + head * D + lane * PER;
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int e = 0; e < PER; ++e) out[e] = acc[e] / lsum;
+      for (int e = 0; e < PER; ++e) v[u][e] = o[(size_t)(t + u) * D + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wsh[h][t + u], v[u][e], acc[e]);
   }
+  for (; t < n; ++t)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wsh[h][t], o[(size_t)t * D + e], acc[e]);
+  const float inv = 1.f / lt;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) store_out<BF16>(outp, head * D + lane * PER + e, acc[e] * inv);
 }
 
 template <bool BF16, int D, int G>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
-  constexpr int U = 4;
-  const float qscale = a.scale * kLog2e;
-  dim3 grid1(a.plan.splits, a.Hkv, a.B);
-  decode_split_kernel<BF16, D, G, U><<<grid1, kDecodeThreads, 0, stream>>>(
-      a.q, a.k, a.v, a.seq_lens, a.position_id, a.ws_ml, a.ws_o, a.Hq, a.Hkv,
-      a.max_length, a.plan.split_rows, a.plan.splits, qscale);
+  dim3 grid(a.Hkv, a.B, a.plan.splits);
+  if constexpr (BF16) {
+    decode_bf16_kernel<D, G><<<grid, kThreads, 0, stream>>>(
+        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
+        static_cast<const uint16_t *>(a.v), a.seq_lens, a.position_id, a.out,
+        a.ws_ml, a.ws_o, a.Hq, a.Hkv, a.max_length,
+        a.plan.split_rows, a.plan.splits, a.scale * kLog2e);
+  } else {
+    decode_f32_kernel<D, G><<<grid, kThreads, 0, stream>>>(
+        static_cast<const float *>(a.q), static_cast<const float *>(a.k),
+        static_cast<const float *>(a.v), a.seq_lens, a.position_id, a.out,
+        a.ws_ml, a.ws_o, a.Hq, a.Hkv, a.max_length,
+        a.plan.split_rows, a.plan.splits, a.scale * kLog2e);
+  }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 grid2(a.Hq, a.B);
-  decode_combine_kernel<BF16, D><<<grid2, 64, 0, stream>>>(
+  if (e != hipSuccess || a.plan.splits <= 1) return e;
+  decode_combine_kernel<BF16, D, G><<<dim3(a.Hkv, a.B), 64 * G, 0, stream>>>(
       a.ws_ml, a.ws_o, a.seq_lens, a.position_id, a.out, a.Hq, a.max_length,
       a.plan.split_rows, a.plan.splits);
   return hipGetLastError();

@@ -10,6 +10,9 @@ namespace attn {
 
 // Threads per decode split workgroup.
 constexpr int kDecodeThreads = 256;
+// Upper bound on split-KV work items per sequence (the combine kernel keeps
+// one weight per split in LDS).
+constexpr int kDecodeMaxSplits = 1024;
 
 struct DecodePlan {
   int split_rows;  // cache rows per split work item
