@@ -103,8 +103,8 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D,
  *   seq_lens   optional DEVICE array int32[B]: sequence b attends to rows
  *              [0, seq_lens[b]). Values are clamped to [0, max_length] on the
  *              device; length 0 yields a zero output row.
- *   scale      multiplier of q·k; any finite value (the Python binding
- *              passes 1/sqrt(D) when the caller gives none).
+ *   scale      multiplier of q·k, finite and > 0 (the Python binding passes
+ *              1/sqrt(D) when the caller gives none).
  *   split_rows cache rows per split-KV work item (0 = automatic). Forcing it
  *              changes only the reduction order, never the math. At most
  *              1024 splits per sequence: a smaller value is raised to
@@ -137,7 +137,7 @@ int attn_decode(int dtype, const void *q, const void *k_cache,
  *   v_cache    [B][Hkv][max_length][D]; rows [0, prefix_len + Lq) must hold
  *              the prefix and the new tokens' K/V; later rows are never read.
  *   out        [B][Hq][Lq][D]
- *   scale      any finite value (binding default 1/sqrt(D)).
+ *   scale      finite and > 0 (binding default 1/sqrt(D)).
  * Requires 0 <= prefix_len, 0 <= Lq, prefix_len + Lq <= max_length.
  * Supported: D in {64, 128}; Hq % Hkv == 0; B, Hq <= 65535. Lq == 0 or
  * B == 0 is a no-op. */

@@ -77,6 +77,8 @@ def decode(**kw):
     (dict(position_id=8192), E_ARG),
     (dict(scale=float("nan")), E_ARG),
     (dict(scale=float("inf")), E_ARG),
+    (dict(scale=0.0), E_ARG),
+    (dict(scale=-0.5), E_ARG),
     (dict(split_rows=-5), E_ARG),
     (dict(q=None), E_ARG),
     (dict(k=None), E_ARG),
@@ -144,6 +146,8 @@ def prefill(**kw):
     (dict(prefix_len=3073), E_ARG),     # prefix + Lq > max_length
     (dict(max_length=0), E_ARG),
     (dict(scale=float("nan")), E_ARG),
+    (dict(scale=0.0), E_ARG),
+    (dict(scale=-1.0), E_ARG),
     (dict(q=None), E_ARG),
     (dict(out=P + 2), E_ARG),
 ])

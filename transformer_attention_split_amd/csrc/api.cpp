@@ -165,8 +165,8 @@ int attn_decode(int dtype, const void *q, const void *k_cache,
   if (seq_lens == nullptr && (position_id < 0 || position_id >= max_length))
     return fail(ATTN_E_ARG, "attn_decode: position_id=%d outside [0, max_length=%d)",
                 position_id, max_length);
-  if (!std::isfinite(scale))
-    return fail(ATTN_E_ARG, "attn_decode: scale is not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_E_ARG, "attn_decode: scale must be finite and > 0");
   if (split_rows < 0)
     return fail(ATTN_E_ARG, "attn_decode: split_rows=%d < 0", split_rows);
   if (B == 0) return ok();  // empty batch: nothing is read or written
@@ -236,8 +236,8 @@ int attn_prefill(int dtype, const void *q, const void *k_cache,
   if (!fits({(double)B, (double)Hkv, (double)max_length, (double)D, 2.0}) ||
       !fits({(double)B, (double)Hq, (double)max_length, (double)D, 2.0}))
     return fail(ATTN_E_ARG, "attn_prefill: extents overflow");
-  if (!std::isfinite(scale))
-    return fail(ATTN_E_ARG, "attn_prefill: scale is not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_E_ARG, "attn_prefill: scale must be finite and > 0");
   if (B == 0 || Lq == 0) return ok();  // nothing is read or written
   if (!q || !k_cache || !v_cache || !out)
     return fail(ATTN_E_ARG, "attn_prefill: null data pointer");

@@ -7,27 +7,35 @@
 // score matrix never reaches HBM. New token i sits at cache row prefix+i and
 // sees rows [0, prefix+i].
 //
-// One workgroup = 4 waves = 64 queries (16 per wave) of one head, walking
-// 64-key tiles up to the causal bound of its last query.
-//   * Block -> work map: workgroup id i runs on XCD i % 8. Every query tile
-//     of one head goes to the same XCD, so the head's K and V are fetched
-//     from HBM once into that XCD's L2 and re-read from there by its 16
-//     query tiles; on each XCD the tiles run longest (most keys) first.
-//   * K is read straight from L1/L2 into the A-operand registers of
-//     v_mfma_f32_16x16x32_bf16 (16 key rows x 32 dims per instruction); V is
-//     staged once per tile in LDS, transposed (d-major), shared by the 4 waves
-//     and double-buffered. The next tile's K and V loads are issued before the
-//     current tile is computed.
+// One workgroup = 8 waves = 2 query groups of one head, walking the 64-key
+// tiles up to the causal bound of its last query:
+//   * Waves: query group qg = w / 4 x key quarter kq = w % 4 (tiles t with
+//     t % 4 == kq). A wave holds NB 16-query column blocks (2 at D = 64: every
+//     K and V operand feeds two MFMAs, halving operand traffic per FLOP; 1 at
+//     D = 128, for the register budget). Two waves per SIMD hide each other's
+//     latencies and overlap one's matrix work with the other's softmax. The
+//     four key quarters of a query group are merged (log-sum-exp) in LDS at
+//     the end.
+//   * Block -> work map: workgroup id i runs on XCD i % 8; every query tile of
+//     one head goes to the same XCD, so the head's K and V are fetched from
+//     HBM once into that XCD's L2; on each XCD tiles run longest first.
+//   * K is read straight from L1/L2 into the A operand of
+//     v_mfma_f32_16x16x32_bf16 (16 key rows x 32 dims per instruction). V is
+//     copied row-major into LDS for all four tiles of an iteration
+//     (double-buffered) and read back with the transposing LDS read
+//     ds_read_b64_tr_b16, which delivers the d-major A operand of the P·V
+//     product directly; the next iteration's V (and, for D = 64, K) loads are
+//     issued before the current one is computed.
 //   * Sᵀ = K·Qᵀ puts each lane on one query and 4 keys of every 16-key block:
-//     the exact operand layout of Oᵀ += Vᵀ·Pᵀ, so P never leaves registers.
-//   * Softmax in the exp2 domain: the running max is kept on the raw scores
+//     the operand layout of Oᵀ += Vᵀ·Pᵀ, so P never leaves registers.
+//   * Softmax in the exp2 domain: the running max is kept on raw scores
 //     (scale > 0 commutes with max), p = exp2(fma(s, scale*log2 e, -m)); the
-//     output is rescaled only when the running max grows by more than 8 (in
-//     log2 units), so p stays below 2^8 and most tiles skip the rescale. Row
-//     sums come from the matrix cores too: an all-ones A operand times Pᵀ
-//     gives every query's sum of the same bf16 probabilities the output uses.
+//     output is rescaled only when the running max grows by more than 8 (log2
+//     units), so p stays below 2^8 and most tiles skip the rescale. Row sums
+//     come from the matrix cores: an all-ones A operand times Pᵀ sums the same
+//     bf16 probabilities the output uses.
 //   * Only tiles that cross the diagonal evaluate the mask; tiles past a
-//     wave's last visible key are skipped.
+//     query group's last visible key are skipped.
 #include "common.h"
 #include "launch.h"
 
@@ -39,9 +47,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 64;  // queries per workgroup
-constexpr int BN = 64;  // keys per tile
-constexpr int kThreads = 256;
+constexpr int BN = 64;   // keys per tile
+constexpr int NKQ = 4;   // key quarters (waves per query group)
+constexpr int NQG = 2;   // query groups per workgroup
+constexpr int kThreads = 512;
 constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag
 
@@ -49,14 +58,33 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// ds_read_b64_tr_b16: in each group of 16 lanes, the 16 addresses name 16
+// runs of 4 bf16 values M[s][0..3]; lane i receives M[i/4 + 4e][i%4] for
+// e = 0..3 (a 4x4-blocked transpose).
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+__device__ __forceinline__ u32x2_t read_tr16(const uint16_t *lds) {
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t *)(const_cast<uint16_t *>(lds)));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
 template <int D>
 struct Tile {
+  static constexpr int NB = D <= 64 ? 2 : 1;  // 16-query column blocks per wave
+  static constexpr int NQW = 16 * NB;         // queries per wave
+  static constexpr int BM = NQG * NQW;        // queries per workgroup
   static constexpr int KS = D / 32;    // MFMA k-steps of K·Qᵀ
   static constexpr int NDB = D / 16;   // 16-wide output blocks
   static constexpr int NKB = BN / 16;  // 16-key blocks per tile
-  static constexpr int SV = BN + 4;    // Vᵀ row stride in LDS (elements)
-  static constexpr int VCH = (BN / 2) * (D / 8) / kThreads;  // V items per thread
-  static_assert(VCH >= 1, "tile too small for the workgroup");
+  static constexpr int SV = D + 16;    // V row stride in LDS (elements): the
+                                       // 4 rows of one transposing read start
+                                       // 8 banks apart
+  static constexpr int VT = BN * SV;   // elements of one V tile
+  static constexpr bool PREFETCH_K = D <= 64;              // register budget
+  static constexpr int LDS_V = 2 * NKQ * VT * 2;           // bytes, 2 buffers
+  static constexpr int LDS_MERGE = (NQG * NKQ * NQW * D + 2 * NQG * NKQ * NQW) * 4;
+  static constexpr int LDS = LDS_V > LDS_MERGE ? LDS_V : LDS_MERGE;
 };
 
 template <int D>
@@ -67,7 +95,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     int n_qtiles, int heads_per_xcd) {
   using T = Tile<D>;
   constexpr int KS = T::KS, NDB = T::NDB, NKB = T::NKB, SV = T::SV;
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * SV];
+  constexpr int NB = T::NB, NQW = T::NQW, BM = T::BM;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint16_t *Vt = reinterpret_cast<uint16_t *>(smem);  // [2][NKQ][BN][SV]
 
   // ---- work item: (head instance, query tile) -----------------------------------
   const int id = blockIdx.x;
@@ -85,193 +115,271 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int l = tid % 64;
   const int li = l % 16;
   const int lg = l / 16;
+  const int kq = w % NKQ;   // key quarter
+  const int qgi = w / NKQ;  // query group
 
   const int kv_len = prefix + Lq;
   const int q_end = min((qt + 1) * BM, Lq);
   const int n_tiles = (prefix + q_end + BN - 1) / BN;
-  const int qw0 = qt * BM + w * 16;     // first query of this wave
-  const int qme = qw0 + li;             // this lane's query
-  const bool w_active = qw0 < Lq;
-  const int w_kmax = prefix + min(qw0 + 15, Lq - 1);  // last key the wave sees
-  const int jlim = prefix + qme;        // last key this lane's query sees
+  const int n_iter = (n_tiles + NKQ - 1) / NKQ;
+  const int qg0 = qt * BM + qgi * NQW;  // first query of this wave's group
+  const bool g_active = qg0 < Lq;
+  const int g_kmax = prefix + min(qg0 + NQW - 1, Lq - 1);  // last visible key
 
   const size_t kvbase = ((size_t)b * Hkv + kvh) * (size_t)max_length * D;
   const uint16_t *kbase = kg + kvbase;
   const uint16_t *vbase = vg + kvbase;
 
-  bf16x8_t qf[KS];
-  {
+  // This wave's queries as B operands (column li of block nb).
+  bf16x8_t qf[NB][KS];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int qme = qg0 + nb * 16 + li;
     const size_t qrow = ((size_t)j * Lq + (size_t)qme) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t v = {0u, 0u, 0u, 0u};
       if (qme < Lq) v = *reinterpret_cast<const u32x4_t *>(qg + qrow + ks * 32 + 8 * lg);
-      qf[ks] = as_bf16x8(v);
+      qf[nb][ks] = as_bf16x8(v);
     }
   }
   const u32x4_t ones_w = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   const bf16x8_t ones = as_bf16x8(ones_w);
 
-  f32x4_t o[NDB];
+  f32x4_t o[NB][NDB];
+  f32x4_t lacc[NB];
+  float mc[NB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};  // row sums (4 identical copies)
-  float mc = kNegInf;                   // running max, scaled (log2 units)
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) o[nb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    lacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mc[nb] = kNegInf;
+  }
 
-  u32x4_t kf[NKB][KS];
-  u32x4_t vreg[T::VCH][2];
+  // K rows (A operands) and V rows are loaded from clamped row indices:
+  // rows at or past kv_len only occur in tiles that cross the diagonal,
+  // where every real query masks them (p = 0), so any finite cache row will
+  // do and no load needs a guard; rows past kv_len are never read.
+  const u32x4_t *k4 = reinterpret_cast<const u32x4_t *>(kbase);
+  const u32x4_t *v4 = reinterpret_cast<const u32x4_t *>(vbase);
+  const unsigned last_row = (unsigned)(kv_len - 1);
 
   auto load_k = [&](int t, u32x4_t (&dst)[NKB][KS]) {
-    const int j0 = t * BN;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int row = j0 + kb * 16 + li;
+      const unsigned row = min((unsigned)(t * BN + kb * 16 + li), last_row);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (row < kv_len)
-          v = *reinterpret_cast<const u32x4_t *>(kbase + (size_t)row * D + ks * 32 + 8 * lg);
-        dst[kb][ks] = v;
-      }
+      for (int ks = 0; ks < KS; ++ks) dst[kb][ks] = k4[row * (D / 8) + ks * 4 + lg];
     }
   };
-  auto load_v = [&](int t) {
-    const int j0 = t * BN;
+  // V of the NKQ tiles of one iteration, copied row-major into LDS: item =
+  // (tile, row, 8-dim chunk), chunks fastest, so one load instruction covers
+  // whole rows and one 16-byte LDS write per item.
+  constexpr int VITEMS = NKQ * BN * (D / 8);
+  constexpr int VCH = VITEMS / kThreads;   // items per thread
+  static_assert(VITEMS % kThreads == 0, "V items per thread");
+  u32x4_t vreg[VCH];
+  auto load_v = [&](int it) {
 #pragma unroll
-    for (int i = 0; i < T::VCH; ++i) {
+    for (int i = 0; i < VCH; ++i) {
       const int c = tid + i * kThreads;
-      const int col = (c % (D / 8)) * 8;
-      const int r0 = j0 + 2 * (c / (D / 8));
-      u32x4_t a = {0u, 0u, 0u, 0u}, bb = {0u, 0u, 0u, 0u};
-      if (r0 < kv_len)
-        a = *reinterpret_cast<const u32x4_t *>(vbase + (size_t)r0 * D + col);
-      if (r0 + 1 < kv_len)
-        bb = *reinterpret_cast<const u32x4_t *>(vbase + (size_t)(r0 + 1) * D + col);
-      vreg[i][0] = a;
-      vreg[i][1] = bb;
+      const int col = c % (D / 8);
+      const int row = (c / (D / 8)) % BN;
+      const int tl = c / (BN * (D / 8));
+      const unsigned r = (unsigned)((it * NKQ + tl) * BN + row);
+      vreg[i] = v4[min(r, last_row) * (D / 8) + col];
     }
   };
   auto store_v = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < T::VCH; ++i) {
+    for (int i = 0; i < VCH; ++i) {
       const int c = tid + i * kThreads;
-      const int col = (c % (D / 8)) * 8;
-      const int p = c / (D / 8);  // row pair inside the tile
-      const u32x4_t a = vreg[i][0], bb = vreg[i][1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (a[e] & 0xffffu) | (bb[e] << 16);
-        const uint32_t hi = (a[e] >> 16) | (bb[e] & 0xffff0000u);
-        *reinterpret_cast<uint32_t *>(&Vt[buf][(col + 2 * e) * SV + 2 * p]) = lo;
-        *reinterpret_cast<uint32_t *>(&Vt[buf][(col + 2 * e + 1) * SV + 2 * p]) = hi;
-      }
+      const int col = c % (D / 8);
+      const int row = (c / (D / 8)) % BN;
+      const int tl = c / (BN * (D / 8));
+      *reinterpret_cast<u32x4_t *>(Vt + (size_t)(buf * NKQ + tl) * T::VT +
+                                   row * SV + col * 8) = vreg[i];
     }
   };
 
-  load_v(0);
-  load_k(0, kf);
-  store_v(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < n_tiles;
-    u32x4_t kn[NKB][KS];
-    if (more) {
-      load_v(t + 1);
-      load_k(t + 1, kn);
-    }
+  // One iteration: this wave's tile of iteration `it` with K operands `kc`;
+  // the next iteration's V (and, for D = 64, K into `kx`) is prefetched.
+  auto step = [&](int it, u32x4_t (&kc)[NKB][KS], u32x4_t (&kx)[NKB][KS]) {
+    // Loads and the LDS store run unconditionally (row indices are clamped,
+    // so the extra loads of the last iteration stay in bounds): with no
+    // branch around them the compiler's wait counts cover exactly the
+    // previous iteration's loads and the prefetch overlaps this iteration.
+    const int buf = it & 1;
+    const int t = it * NKQ + kq;
+    const int tn = t + NKQ;
+    load_v(it + 1);
+    if constexpr (T::PREFETCH_K) load_k(tn, kx);
     const int j0 = t * BN;
-    if (w_active && j0 <= w_kmax) {
-      // ---- Sᵀ = K·Qᵀ (raw scores) ----------------------------------------------------
-      f32x4_t s[NKB];
+    if (t < n_tiles && g_active && j0 <= g_kmax) {
+      const uint16_t *vt = Vt + (size_t)(buf * NKQ + kq) * T::VT;
+      // ---- Sᵀ = K·Qᵀ (raw scores), every K operand feeds NB query blocks ----
+      f32x4_t s[NB][NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kb][ks]),
-                                                         qf[ks], s[kb], 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb) s[nb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8_t a = as_bf16x8(kc[kb][ks]);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            s[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[nb][kb], 0, 0, 0);
+        }
       }
-      // ---- causal mask (diagonal tiles only) and row max ---------------------
-      if (j0 + BN - 1 > prefix + qw0) {
+      const bool diag = j0 + BN - 1 > prefix + qg0;
+      bf16x8_t pb[NB][BN / 32];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+      for (int nb = 0; nb < NB; ++nb) {
+        // ---- causal mask (diagonal tiles only) -----------------------------------
+        if (diag) {
+          // key j0 + 16 kb + 4 lg + r is visible iff 16 kb + r <= lim
+          const int lim = prefix + qg0 + nb * 16 + li - j0 - 4 * lg;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (j0 + kb * 16 + 4 * lg + r > jlim) s[kb][r] = kNegInf;
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (16 * kb + r > lim) s[nb][kb][r] = kNegInf;
+        }
+        // ---- running max over the 4 lanes of the query; lazy rescale ---------
+        float m0 = fmaxf(fmaxf(s[nb][0][0], s[nb][0][1]), fmaxf(s[nb][0][2], s[nb][0][3]));
+#pragma unroll
+        for (int kb = 1; kb < NKB; ++kb)
+          m0 = fmaxf(fmaxf(m0, fmaxf(s[nb][kb][0], s[nb][kb][1])),
+                     fmaxf(s[nb][kb][2], s[nb][kb][3]));
+        m0 = fmaxf(m0, __shfl_xor(m0, 16));
+        m0 = fmaxf(m0, __shfl_xor(m0, 32));
+        const float mloc_c = m0 * qk_scale;
+        if (__any(mloc_c > mc[nb] + kRescaleSlack)) {
+          const float mnew = fmaxf(mc[nb], mloc_c);
+          // a query with no visible key yet keeps max -inf: no rescale (and
+          // no -inf - -inf)
+          const float alpha = mnew == mc[nb] ? 1.f : fast_exp2(mc[nb] - mnew);
+          mc[nb] = mnew;
+          lacc[nb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) o[nb][db] *= alpha;
+        }
+        // every score of a query with max -inf is masked: any finite offset
+        // gives p = 0 (and -mc would be +inf)
+        const float nmc = mc[nb] == kNegInf ? 0.f : -mc[nb];
+#pragma unroll
+        for (int t2 = 0; t2 < BN / 32; ++t2) {
+          float p[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[r] = fast_exp2(fmaf(s[nb][2 * t2][r], qk_scale, nmc));
+            p[4 + r] = fast_exp2(fmaf(s[nb][2 * t2 + 1][r], qk_scale, nmc));
+          }
+          const u32x4_t pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                              pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+          pb[nb][t2] = as_bf16x8(pw);
+        }
       }
-      float mloc = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        mloc = fmaxf(fmaxf(mloc, fmaxf(s[kb][0], s[kb][1])), fmaxf(s[kb][2], s[kb][3]));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float mloc_c = mloc * qk_scale;
-      if (__any(mloc_c > mc + kRescaleSlack)) {
-        const float mnew = fmaxf(mc, mloc_c);
-        const float alpha = fast_exp2(mc - mnew);
-        mc = mnew;
-        lacc *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      }
-      // ---- P, row sums and Oᵀ += Vᵀ·Pᵀ ----------------------------------------
-      const float nmc = -mc;
+      // ---- row sums and Oᵀ += Vᵀ·Pᵀ, every V operand feeds NB query blocks ---
 #pragma unroll
       for (int t2 = 0; t2 < BN / 32; ++t2) {
-        float p[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[r] = fast_exp2(fmaf(s[2 * t2][r], qk_scale, nmc));
-          p[4 + r] = fast_exp2(fmaf(s[2 * t2 + 1][r], qk_scale, nmc));
-        }
-        const u32x4_t pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-        const bf16x8_t pb = as_bf16x8(pw);
-        lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb, lacc, 0, 0, 0);
+        for (int nb = 0; nb < NB; ++nb)
+          lacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[nb][t2], lacc[nb], 0, 0, 0);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const uint16_t *vrow = &Vt[buf][(db * 16 + li) * SV + 32 * t2 + 4 * lg];
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 16);
+          // transposing reads: lane li of lane group lg receives
+          // V[key][16 db + li] for keys 32 t2 + 4 lg + 0..3 and + 16
+          const uint16_t *src = vt + (32 * t2 + 4 * lg + li / 4) * SV + db * 16 + 4 * (li % 4);
+          const u32x2_t lo = read_tr16(src);
+          const u32x2_t hi = read_tr16(src + 16 * SV);
           const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
-          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), pb,
-                                                         o[db], 0, 0, 0);
+          const bf16x8_t a = as_bf16x8(av);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nb][t2], o[nb][db], 0, 0, 0);
         }
       }
     }
-    if (more) {
-      store_v(buf ^ 1);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[kb][ks] = kn[kb][ks];
-    }
+    store_v(buf ^ 1);
+    if constexpr (!T::PREFETCH_K) load_k(tn, kx);
     __syncthreads();
+  };
+
+  u32x4_t kfa[NKB][KS];
+  load_v(0);
+  load_k(kq, kfa);
+  store_v(0);
+  __syncthreads();
+  if constexpr (T::PREFETCH_K) {
+    // two register sets alternate roles (no copies)
+    u32x4_t kfb[NKB][KS];
+    for (int it = 0; it < n_iter; it += 2) {
+      step(it, kfa, kfb);
+      if (it + 1 < n_iter) step(it + 1, kfb, kfa);
+    }
+  } else {
+    // the next tile's K is loaded into the same registers after use
+    for (int it = 0; it < n_iter; ++it) step(it, kfa, kfa);
   }
 
-  // ---- finalise: divide by the row sum, store bf16 -------------------------------
-  if (qme < Lq) {
-    const float inv = 1.f / lacc[0];
-    uint16_t *orow = outg + ((size_t)j * Lq + (size_t)qme) * D;
+  // ---- merge the key quarters of each query group (log-sum-exp), store -----------
+  float *mo = reinterpret_cast<float *>(smem);         // [NQG][NKQ][NQW][D]
+  float *mm = mo + NQG * NKQ * NQW * D;                // [NQG][NKQ][NQW]
+  float *ml = mm + NQG * NKQ * NQW;                    // [NQG][NKQ][NQW]
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const u32x2_t wv = {pack_bf16x2(o[db][0] * inv, o[db][1] * inv),
-                          pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
-      *reinterpret_cast<u32x2_t *>(orow + db * 16 + 4 * lg) = wv;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int qi = nb * 16 + li;  // query inside the group
+    float *dst = mo + ((size_t)(qgi * NKQ + kq) * NQW + qi) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4_t *>(dst + db * 16 + 4 * lg) = o[nb][db];
+    if (lg == 0) {
+      mm[(qgi * NKQ + kq) * NQW + qi] = mc[nb];
+      ml[(qgi * NKQ + kq) * NQW + qi] = lacc[nb][0];
     }
+  }
+  __syncthreads();
+  for (int i = tid; i < BM * D / 2; i += kThreads) {
+    const int q = (2 * i) / D;       // query inside the workgroup
+    const int d = (2 * i) % D;       // even dimension; this thread does d, d+1
+    const int grp = q / NQW, qi = q % NQW;
+    const int qglob = qt * BM + q;
+    if (qglob >= Lq) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int kk = 0; kk < NKQ; ++kk) M = fmaxf(M, mm[(grp * NKQ + kk) * NQW + qi]);
+    float a0 = 0.f, a1 = 0.f, lt = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKQ; ++kk) {
+      const float wgt = fast_exp2(mm[(grp * NKQ + kk) * NQW + qi] - M);
+      const float *src = mo + ((size_t)(grp * NKQ + kk) * NQW + qi) * D + d;
+      a0 = fmaf(wgt, src[0], a0);
+      a1 = fmaf(wgt, src[1], a1);
+      lt = fmaf(wgt, ml[(grp * NKQ + kk) * NQW + qi], lt);
+    }
+    const float inv = 1.f / lt;
+    *reinterpret_cast<uint32_t *>(outg + ((size_t)j * Lq + qglob) * D + d) =
+        pack_bf16x2(a0 * inv, a1 * inv);
   }
 }
 
 template <int D>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
-  const int n_qtiles = (a.Lq + BM - 1) / BM;
+  using T = Tile<D>;
+  const int n_qtiles = (a.Lq + T::BM - 1) / T::BM;
   const int NH = a.B * a.Hq;
   const int heads_per_xcd = (NH + kXcds - 1) / kXcds;
   const long blocks = (long)kXcds * heads_per_xcd * n_qtiles;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  prefill_kernel<D><<<dim3((unsigned)blocks), kThreads, 0, stream>>>(
+  if (T::LDS > 65536) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&prefill_kernel<D>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+    if (e != hipSuccess) return e;
+  }
+  prefill_kernel<D><<<dim3((unsigned)blocks), kThreads, T::LDS, stream>>>(
       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
       static_cast<const uint16_t *>(a.v), static_cast<uint16_t *>(a.out), NH,
       a.Hq, a.Hkv, a.max_length, a.Lq, a.prefix_len, a.scale * kLog2e,
