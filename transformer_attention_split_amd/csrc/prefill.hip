@@ -58,6 +58,14 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// max of three fp32 values in one v_max3_f32 (no operand quieting: the
+// kernel's scores are never NaN).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // ds_read_b64_tr_b16: in each group of 16 lanes, the 16 addresses name 16
 // runs of 4 bf16 values M[s][0..3]; lane i receives M[i/4 + 4e][i%4] for
 // e = 0..3 (a 4x4-blocked transpose).
@@ -143,6 +151,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       qf[nb][ks] = as_bf16x8(v);
     }
   }
+  // byte addresses of lanes l ^ 16 and l ^ 32 for ds_bpermute
+  const int bp16 = (l ^ 16) * 4;
+  const int bp32 = (l ^ 32) * 4;
   const u32x4_t ones_w = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
   const bf16x8_t ones = as_bf16x8(ones_w);
 
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         // ---- causal mask (diagonal tiles only) -----------------------------------
-        if (diag) {
+        if (diag) [[unlikely]] {
           // key j0 + 16 kb + 4 lg + r is visible iff 16 kb + r <= lim
           const int lim = prefix + qg0 + nb * 16 + li - j0 - 4 * lg;
 #pragma unroll
@@ -247,15 +258,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
               if (16 * kb + r > lim) s[nb][kb][r] = kNegInf;
         }
         // ---- running max over the 4 lanes of the query; lazy rescale ---------
-        float m0 = fmaxf(fmaxf(s[nb][0][0], s[nb][0][1]), fmaxf(s[nb][0][2], s[nb][0][3]));
+        float m0 = max3(s[nb][0][0], s[nb][0][1], s[nb][0][2]);
+        m0 = max3(m0, s[nb][0][3], s[nb][1][0]);
 #pragma unroll
-        for (int kb = 1; kb < NKB; ++kb)
-          m0 = fmaxf(fmaxf(m0, fmaxf(s[nb][kb][0], s[nb][kb][1])),
-                     fmaxf(s[nb][kb][2], s[nb][kb][3]));
-        m0 = fmaxf(m0, __shfl_xor(m0, 16));
-        m0 = fmaxf(m0, __shfl_xor(m0, 32));
+        for (int kb = 1; kb < NKB; ++kb) {
+          m0 = max3(m0, s[nb][kb][1], s[nb][kb][2]);
+          m0 = kb + 1 < NKB ? max3(m0, s[nb][kb][3], s[nb][kb + 1][0])
+                            : fmaxf(m0, s[nb][kb][3]);
+        }
+        m0 = fmaxf(m0, __int_as_float(__builtin_amdgcn_ds_bpermute(bp16, __float_as_int(m0))));
+        m0 = fmaxf(m0, __int_as_float(__builtin_amdgcn_ds_bpermute(bp32, __float_as_int(m0))));
         const float mloc_c = m0 * qk_scale;
-        if (__any(mloc_c > mc[nb] + kRescaleSlack)) {
+        if (__any(mloc_c > mc[nb] + kRescaleSlack)) [[unlikely]] {
           const float mnew = fmaxf(mc[nb], mloc_c);
           // a query with no visible key yet keeps max -inf: no rescale (and
           // no -inf - -inf)
