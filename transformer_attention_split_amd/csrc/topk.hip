@@ -14,18 +14,21 @@
 //      B = 16 key rows per block; the 64 dimensions are spread as 16 MFMAs of
 //      4), written to LDS. Waves take key blocks round-robin.
 //   2. select, one row per wave at a time, lane e holding keys e, e+64, ...:
-//      a) the k-th largest fp32-rounded score T by bisection over the 32-bit
-//         order-preserving key, counting with wave ballots; every score whose
-//         fp32 key exceeds T is in (rounding is monotone);
-//      b) only if more scores share T than places remain, the same bisection
-//         over the exact 64-bit keys of those candidates, and remaining ties
-//         are filled in ascending key index.
+//      a) the k-th largest fp32-rounded score T by a most-significant-digit
+//         radix select over the 32-bit order-preserving key: four passes of
+//         8 bits, each a 256-bin LDS histogram of the keys still sharing the
+//         prefix, a wave prefix sum over the bins from the top and a ballot
+//         for the bin holding the k-th key. Every score whose fp32 key
+//         exceeds T is in (rounding is monotone);
+//      b) only if more scores share T than places remain, a bisection over
+//         the exact 64-bit keys of those candidates, and remaining ties are
+//         filled in ascending key index.
 //      The chosen (index, score) pairs are compacted in ascending index order
 //      (into the row's own LDS storage and a per-wave index list).
 //   3. gather: lanes = 4 slot groups x 16 groups of 4 dimensions; each slot
 //      group walks every 4th selected key and adds score * v[key] in fp64
-//      (one coalesced 256-byte row read per key per slot group); the four
-//      partial sums are added across lanes and rounded to fp32.
+//      (one coalesced 256-byte row read per key per slot group, 16 in flight);
+//      the four partial sums are added across lanes and rounded to fp32.
 #include "common.h"
 #include "launch.h"
 
@@ -42,6 +45,22 @@ __device__ __forceinline__ uint32_t order32(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Inclusive prefix sum over the 64 lanes: DPP row shifts inside each
+// 16-lane row (out-of-row sources contribute 0), then the totals of the
+// earlier rows read with readlane.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, int lane) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);
+  const uint32_t t0 = __builtin_amdgcn_readlane(x, 15);
+  const uint32_t t1 = __builtin_amdgcn_readlane(x, 31);
+  const uint32_t t2 = __builtin_amdgcn_readlane(x, 47);
+  return x + (lane >= 16 ? t0 : 0u) + (lane >= 32 ? t1 : 0u) + (lane >= 48 ? t2 : 0u);
+}
+
 __device__ __forceinline__ uint64_t order64(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
@@ -56,6 +75,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   double *S = reinterpret_cast<double *>(smem);                 // [QB][NP]
   int *jl = reinterpret_cast<int *>(smem + (size_t)QB * NP * 8);  // [4][NP]
+  __shared__ __attribute__((aligned(16))) uint32_t hst[4 * 256];     // per-wave histograms
+  for (int i = threadIdx.x; i < 4 * 256; i += kThreads) hst[i] = 0u;
 
   const int q0 = blockIdx.x * QB;
   const size_t bh = (size_t)blockIdx.z * H + blockIdx.y;
@@ -88,25 +109,33 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
       }
     }
     const int nkb = (n + 15) / 16;
-    for (int blk = w; blk < nkb; blk += 4) {
-      const int kr = blk * 16 + li;
-      float4 x[4] = {};
-      if (kr < n) {
+    // K rows of the next block are loaded (from a clamped, in-bounds row)
+    // while the current block runs on the matrix cores.
+    auto load_kblk = [&](int blk, float4 (&x)[4]) {
+      const int kr = min(blk * 16 + li, n - 1);
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          x[c] = *reinterpret_cast<const float4 *>(kb + (size_t)kr * DIM + 16 * lg + 4 * c);
-      }
+      for (int c = 0; c < 4; ++c)
+        x[c] = *reinterpret_cast<const float4 *>(kb + (size_t)kr * DIM + 16 * lg + 4 * c);
+    };
+    float4 xc[4], xn[4];
+    load_kblk(w, xc);
+    for (int blk = w; blk < nkb; blk += 4) {
+      load_kblk(blk + 4 < nkb ? blk + 4 : blk, xn);
+      const bool kvalid = blk * 16 + li < n;
       f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 0], (double)x[c].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 1], (double)x[c].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 2], (double)x[c].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 3], (double)x[c].w, acc, 0, 0, 0);
+        const float4 x = kvalid ? xc[c] : float4{0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 0], (double)x.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 1], (double)x.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 2], (double)x.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 3], (double)x.w, acc, 0, 0, 0);
       }
       // lane l, register r holds query row lg + 4r, key blk*16 + li
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[(lg + 4 * r) * NP + blk * 16 + li] = acc[r];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xc[c] = xn[c];
     }
   }
   __syncthreads();
@@ -128,22 +157,56 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
         s[t] = ok ? S[i * NP + j] + 0.0 : 0.0;  // +0.0 turns -0 into +0
         k32[t] = ok ? order32((float)s[t] + 0.0f) : 0u;
       }
-      uint32_t T = 0;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
-        int cnt = 0;
+      // k-th largest 32-bit key by 4 radix passes of 8 bits, most
+      // significant first: histogram the candidates' digit in LDS, scan
+      // the bins from the top, keep the bin that holds the k-th key.
+      uint32_t T = 0;        // key prefix found so far
+      int krem = topk;       // rank still to find inside the prefix
+      int gt = 0;            // keys above the prefix
+      int nc = 0;            // keys equal to the final key
+      uint32_t *hist = hst + w * 256;
 #pragma unroll
-        for (int t = 0; t < NTP; ++t) cnt += __popcll(__ballot(k32[t] >= cand));
-        if (cnt >= topk) T = cand;
+      for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+#pragma unroll
+        for (int t = 0; t < NTP; ++t) {
+          const bool cand = k32[t] != 0u &&
+                            (pass == 0 || (k32[t] >> (shift + 8)) == T);
+          if (cand) atomicAdd(&hist[(k32[t] >> shift) & 0xffu], 1u);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane l holds bins 255-4l (top) .. 252-4l
+        const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(&hist[252 - 4 * l]);
+        const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
+        const uint32_t incl = wave_inclusive_scan(local, l);
+        const uint64_t hit = __ballot(incl >= (uint32_t)krem);
+        const int L = __ffsll((unsigned long long)hit) - 1;
+        uint32_t c = __builtin_amdgcn_readlane(incl - local, L);
+        const uint32_t h3 = __builtin_amdgcn_readlane(hv[3], L);
+        const uint32_t h2 = __builtin_amdgcn_readlane(hv[2], L);
+        const uint32_t h1 = __builtin_amdgcn_readlane(hv[1], L);
+        const uint32_t h0 = __builtin_amdgcn_readlane(hv[0], L);
+        int bin, hb;
+        if (c + h3 >= (uint32_t)krem) { bin = 255 - 4 * L; hb = h3; }
+        else if ((c += h3) + h2 >= (uint32_t)krem) { bin = 254 - 4 * L; hb = h2; }
+        else if ((c += h2) + h1 >= (uint32_t)krem) { bin = 253 - 4 * L; hb = h1; }
+        else { c += h1; bin = 252 - 4 * L; hb = h0; }
+        krem -= (int)c;
+        gt += (int)c;
+        T = (T << 8) | (uint32_t)bin;
+        nc = hb;
+        *reinterpret_cast<u32x4_t *>(&hist[252 - 4 * l]) = u32x4_t{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
       uint64_t selm[NTP], cm[NTP];
-      int gt = 0, nc = 0;
 #pragma unroll
       for (int t = 0; t < NTP; ++t) {
         selm[t] = __ballot(k32[t] > T);
         cm[t] = __ballot(k32[t] == T);
-        gt += __popcll(selm[t]);
-        nc += __popcll(cm[t]);
       }
       const int need = topk - gt;  // >= 1
       if (nc == need) {
@@ -202,15 +265,29 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
       const int sg = l / 16;
       const int dq = l % 16;
       double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-      for (int p = sg; p < topk; p += 4) {
-        const int j = jl[w * NP + p];
-        const double sj = S[i * NP + p];
-        const float4 vv = *reinterpret_cast<const float4 *>(vb + (size_t)j * DIM + 4 * dq);
-        acc[0] = fma(sj, (double)vv.x, acc[0]);
-        acc[1] = fma(sj, (double)vv.y, acc[1]);
-        acc[2] = fma(sj, (double)vv.z, acc[2]);
-        acc[3] = fma(sj, (double)vv.w, acc[3]);
+      // chunks of 64 selected keys: each slot group issues its 16 row loads
+      // before accumulating (one memory latency per chunk); slots past topk
+      // read row 0 and add nothing.
+      for (int p0 = 0; p0 < topk; p0 += 64) {
+        float4 vv[16];
+        double sj[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int p = p0 + sg + 4 * u;
+          const bool ok = p < topk;
+          const int j = ok ? jl[w * NP + p] : 0;
+          sj[u] = ok ? S[i * NP + p] : 0.0;
+          vv[u] = *reinterpret_cast<const float4 *>(vb + (size_t)j * DIM + 4 * dq);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (p0 + sg + 4 * u < topk) {
+            acc[0] = fma(sj[u], (double)vv[u].x, acc[0]);
+            acc[1] = fma(sj[u], (double)vv[u].y, acc[1]);
+            acc[2] = fma(sj[u], (double)vv[u].z, acc[2]);
+            acc[3] = fma(sj[u], (double)vv[u].w, acc[3]);
+          }
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
