@@ -161,8 +161,9 @@ int attn_prefill(int dtype, const void *q, const void *k_cache,
  *   q, k, v, out  fp32 [b][h][n][d]
  *   idx_out       optional int32 [b][h][n][topk] (NULL to skip): the selected
  *                 indices of each row in ascending order.
- * Supported: d == 64; 1 <= n <= 1024; 1 <= topk <= n; b, h <= 65535.
- * b == 0 is a no-op. */
+ * Supported: d == 64; 1 <= n <= 1024; 1 <= topk <= n; b, h <= 65535 and
+ * b·h·ceil(n/16) <= 2^23 (one workgroup per 16 rows). b == 0 or h == 0 is a
+ * no-op. */
 int attn_topk(const float *q, const float *k, const float *v, float *out,
               int32_t *idx_out, int b, int h, int n, int d, int topk,
               void *stream);

@@ -178,6 +178,7 @@ def topk(**kw):
     (dict(d=128), E_UNSUP),
     (dict(n=0), E_ARG),
     (dict(n=2048), E_UNSUP),
+    (dict(b=65535, h=65535), E_UNSUP),  # more than 2^23 workgroups
     (dict(topk=0), E_ARG),
     (dict(topk=513), E_ARG),
     (dict(v=None), E_ARG),

@@ -262,6 +262,10 @@ int attn_topk(const float *q, const float *k, const float *v, float *out,
   if (n > 1024) return fail(ATTN_E_UNSUPPORTED, "attn_topk: n=%d > 1024", n);
   if (topk < 1 || topk > n)
     return fail(ATTN_E_ARG, "attn_topk: topk=%d outside [1, n=%d]", topk, n);
+  if ((int64_t)b * h * ((n + 15) / 16) > (int64_t)1 << 23)
+    return fail(ATTN_E_UNSUPPORTED,
+                "attn_topk: b*h*ceil(n/16)=%lld workgroups > 2^23",
+                (long long)b * h * ((n + 15) / 16));
   if (b == 0 || h == 0) return ok();  // nothing is read or written
   if (!q || !k || !v || !out)
     return fail(ATTN_E_ARG, "attn_topk: null data pointer");

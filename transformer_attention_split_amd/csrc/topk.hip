@@ -29,6 +29,8 @@
 //      group walks every 4th selected key and adds score * v[key] in fp64
 //      (one coalesced 256-byte row read per key per slot group, 16 in flight);
 //      the four partial sums are added across lanes and rounded to fp32.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -61,6 +63,13 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, int lane) {
   return x + (lane >= 16 ? t0 : 0u) + (lane >= 32 ? t1 : 0u) + (lane >= 48 ? t2 : 0u);
 }
 
+// LDS writes of the wave become visible to all its lanes.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ uint64_t order64(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
@@ -70,16 +79,22 @@ template <int NTP>
 __global__ __launch_bounds__(kThreads) void topk_kernel(
     const float *__restrict__ qg, const float *__restrict__ kg,
     const float *__restrict__ vg, float *__restrict__ outg,
-    int32_t *__restrict__ idxg, int H, int n, int topk) {
+    int32_t *__restrict__ idxg, int n, int topk, int n_qtiles, int n_work) {
   constexpr int NP = 64 * NTP;  // padded row length
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   double *S = reinterpret_cast<double *>(smem);                 // [QB][NP]
   int *jl = reinterpret_cast<int *>(smem + (size_t)QB * NP * 8);  // [4][NP]
-  __shared__ __attribute__((aligned(16))) uint32_t hst[4 * 256];     // per-wave histograms
+  __shared__ __attribute__((aligned(16))) uint32_t hst[4 * 256];  // per-wave histograms
   for (int i = threadIdx.x; i < 4 * 256; i += kThreads) hst[i] = 0u;
 
-  const int q0 = blockIdx.x * QB;
-  const size_t bh = (size_t)blockIdx.z * H + blockIdx.y;
+  // Workgroup i runs on XCD i % 8. Each XCD takes a contiguous range of the
+  // (b·h, query tile) work list, so the query tiles of one (b, h) share that
+  // XCD's L2 and its K and V are fetched from HBM about once.
+  const int xcd = blockIdx.x % 8;
+  const int per = n_work / 8, extra = n_work % 8;
+  const int work = xcd * per + min(xcd, extra) + (int)(blockIdx.x / 8);
+  const size_t bh = (size_t)(work / n_qtiles);
+  const int q0 = (work % n_qtiles) * QB;
   const float *qb = qg + bh * n * DIM;
   const float *kb = kg + bh * n * DIM;
   const float *vb = vg + bh * n * DIM;
@@ -90,16 +105,16 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   const int lg = l / 16;
 
   // ---- 1. scores ---------------------------------------------------------------
+  // Query rows and key rows past n are read from row n-1 (in bounds); the
+  // scores they produce sit in rows and columns that are never used.
   {
     double qa[16];
     {
-      const int qr = q0 + li;
-      float4 x[4] = {};
-      if (qr < n) {
+      const int qr = min(q0 + li, n - 1);
+      float4 x[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          x[c] = *reinterpret_cast<const float4 *>(qb + (size_t)qr * DIM + 16 * lg + 4 * c);
-      }
+      for (int c = 0; c < 4; ++c)
+        x[c] = *reinterpret_cast<const float4 *>(qb + (size_t)qr * DIM + 16 * lg + 4 * c);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         qa[4 * c + 0] = x[c].x;
@@ -109,33 +124,47 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
       }
     }
     const int nkb = (n + 15) / 16;
-    // K rows of the next block are loaded (from a clamped, in-bounds row)
-    // while the current block runs on the matrix cores.
+    // Two accumulators halve the dependent MFMA chain (the 64-term sum is
+    // split into two halves of 32).
     auto load_kblk = [&](int blk, float4 (&x)[4]) {
       const int kr = min(blk * 16 + li, n - 1);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         x[c] = *reinterpret_cast<const float4 *>(kb + (size_t)kr * DIM + 16 * lg + 4 * c);
     };
-    float4 xc[4], xn[4];
-    load_kblk(w, xc);
-    for (int blk = w; blk < nkb; blk += 4) {
-      load_kblk(blk + 4 < nkb ? blk + 4 : blk, xn);
-      const bool kvalid = blk * 16 + li < n;
-      f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+    auto compute = [&](int blk, const float4 (&x4)[4]) {
+      f64x4_t a0 = {0.0, 0.0, 0.0, 0.0}, a1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float4 x = kvalid ? xc[c] : float4{0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 0], (double)x.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 1], (double)x.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 2], (double)x.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 3], (double)x.w, acc, 0, 0, 0);
+      for (int c = 0; c < 2; ++c) {
+        const float4 x = x4[c], y = x4[c + 2];
+        a0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 0], (double)x.x, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 8], (double)y.x, a1, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 1], (double)x.y, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 9], (double)y.y, a1, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 2], (double)x.z, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 10], (double)y.z, a1, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 3], (double)x.w, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[4 * c + 11], (double)y.w, a1, 0, 0, 0);
       }
       // lane l, register r holds query row lg + 4r, key blk*16 + li
+      if (blk < nkb) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[(lg + 4 * r) * NP + blk * 16 + li] = acc[r];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) xc[c] = xn[c];
+        for (int r = 0; r < 4; ++r) S[(lg + 4 * r) * NP + blk * 16 + li] = a0[r] + a1[r];
+      }
+    };
+    // Two register buffers: each block's rows are loaded one block ahead of
+    // their use. Blocks past the end are computed from clamped rows and not
+    // stored. The scheduling barriers keep the compiler from sinking the
+    // loads down to their use.
+    float4 xa[4], xb[4];
+    load_kblk(w, xa);
+    for (int blk = w; blk < nkb; blk += 8) {
+      load_kblk(blk + 4, xb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(blk, xa);
+      load_kblk(blk + 8, xa);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(blk + 4, xb);
     }
   }
   __syncthreads();
@@ -151,10 +180,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
       double s[NTP];
       uint32_t k32[NTP];
 #pragma unroll
+      for (int t = 0; t < NTP; ++t) s[t] = S[i * NP + l + 64 * t];  // padding too
+#pragma unroll
       for (int t = 0; t < NTP; ++t) {
-        const int j = l + 64 * t;
-        const bool ok = j < n;
-        s[t] = ok ? S[i * NP + j] + 0.0 : 0.0;  // +0.0 turns -0 into +0
+        const bool ok = l + 64 * t < n;
+        s[t] = ok ? s[t] + 0.0 : 0.0;  // +0.0 turns -0 into +0
         k32[t] = ok ? order32((float)s[t] + 0.0f) : 0u;
       }
       // k-th largest 32-bit key by 4 radix passes of 8 bits, most
@@ -174,9 +204,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
                             (pass == 0 || (k32[t] >> (shift + 8)) == T);
           if (cand) atomicAdd(&hist[(k32[t] >> shift) & 0xffu], 1u);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_sync();
         // lane l holds bins 255-4l (top) .. 252-4l
         const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(&hist[252 - 4 * l]);
         const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
@@ -198,9 +226,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
         T = (T << 8) | (uint32_t)bin;
         nc = hb;
         *reinterpret_cast<u32x4_t *>(&hist[252 - 4 * l]) = u32x4_t{0u, 0u, 0u, 0u};
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_sync();
       }
       uint64_t selm[NTP], cm[NTP];
 #pragma unroll
@@ -259,7 +285,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
         before += __popcll(mt);
       }
     }
-    __syncthreads();
+    // From here on every LDS word a wave touches is its own (row i of S and
+    // its index list), so the lanes of the wave only need to see each other.
+    wave_sync();
     if (row_ok) {
       // ---- 3. gather ---------------------------------------------------------------
       const int sg = l / 16;
@@ -267,28 +295,37 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
       double acc[4] = {0.0, 0.0, 0.0, 0.0};
       // chunks of 64 selected keys: each slot group issues its 16 row loads
       // before accumulating (one memory latency per chunk); slots past topk
-      // read row 0 and add nothing.
-      for (int p0 = 0; p0 < topk; p0 += 64) {
+      // read row 0 and contribute nothing.
+      auto chunk = [&](int p0, auto full) {
+        constexpr bool FULL = decltype(full)::value;  // all 64 slots < topk
         float4 vv[16];
         double sj[16];
+        int jr[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {  // p < NP: in bounds, maybe stale
+          jr[u] = jl[w * NP + p0 + sg + 4 * u];
+          sj[u] = S[i * NP + p0 + sg + 4 * u];
+        }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          const int p = p0 + sg + 4 * u;
-          const bool ok = p < topk;
-          const int j = ok ? jl[w * NP + p] : 0;
-          sj[u] = ok ? S[i * NP + p] : 0.0;
+          const int j = (FULL || p0 + sg + 4 * u < topk) ? jr[u] : 0;
           vv[u] = *reinterpret_cast<const float4 *>(vb + (size_t)j * DIM + 4 * dq);
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          if (p0 + sg + 4 * u < topk) {
-            acc[0] = fma(sj[u], (double)vv[u].x, acc[0]);
-            acc[1] = fma(sj[u], (double)vv[u].y, acc[1]);
-            acc[2] = fma(sj[u], (double)vv[u].z, acc[2]);
-            acc[3] = fma(sj[u], (double)vv[u].w, acc[3]);
-          }
+          // a slot past topk adds fma(0, 0, acc) = acc exactly
+          const bool ok = FULL || p0 + sg + 4 * u < topk;
+          const double sv = ok ? sj[u] : 0.0;
+          const float4 x = ok ? vv[u] : float4{0.f, 0.f, 0.f, 0.f};
+          acc[0] = fma(sv, (double)x.x, acc[0]);
+          acc[1] = fma(sv, (double)x.y, acc[1]);
+          acc[2] = fma(sv, (double)x.z, acc[2]);
+          acc[3] = fma(sv, (double)x.w, acc[3]);
         }
-      }
+      };
+      int p0 = 0;
+      for (; p0 + 64 <= topk; p0 += 64) chunk(p0, std::true_type{});
+      if (p0 < topk) chunk(p0, std::false_type{});
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         acc[e] += __shfl_xor(acc[e], 16);
@@ -299,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
         *reinterpret_cast<float4 *>(outg + (bh * n + qr) * DIM + 4 * dq) = o;
       }
     }
-    __syncthreads();
+    wave_sync();
   }
 }
 
@@ -312,9 +349,10 @@ hipError_t launch_ntp(const TopkArgs &a, hipStream_t stream) {
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
-  dim3 grid((a.n + QB - 1) / QB, a.h, a.b);
-  topk_kernel<NTP><<<grid, kThreads, shmem, stream>>>(a.q, a.k, a.v, a.out,
-                                                      a.idx, a.h, a.n, a.topk);
+  const int n_qtiles = (a.n + QB - 1) / QB;
+  const int n_work = n_qtiles * a.h * a.b;  // <= 2^23, checked by the caller
+  topk_kernel<NTP><<<n_work, kThreads, shmem, stream>>>(
+      a.q, a.k, a.v, a.out, a.idx, a.n, a.topk, n_qtiles, n_work);
   return hipGetLastError();
 }
 
