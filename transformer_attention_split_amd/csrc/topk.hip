@@ -180,12 +180,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
       double s[NTP];
       uint32_t k32[NTP];
 #pragma unroll
-      for (int t = 0; t < NTP; ++t) s[t] = S[i * NP + l + 64 * t];  // padding too
-#pragma unroll
       for (int t = 0; t < NTP; ++t) {
+        // computed for every slot (padding too: in bounds, maybe stale) and
+        // then selected, so that no load waits behind a branch
+        const double v = S[i * NP + l + 64 * t] + 0.0;  // +0.0 turns -0 into +0
+        const uint32_t key = order32((float)v + 0.0f);
         const bool ok = l + 64 * t < n;
-        s[t] = ok ? s[t] + 0.0 : 0.0;  // +0.0 turns -0 into +0
-        k32[t] = ok ? order32((float)s[t] + 0.0f) : 0u;
+        s[t] = ok ? v : 0.0;
+        k32[t] = ok ? key : 0u;
       }
       // k-th largest 32-bit key by 4 radix passes of 8 bits, most
       // significant first: histogram the candidates' digit in LDS, scan
