@@ -8,12 +8,16 @@
 // is read once and serves the whole group of G query heads.
 //
 // Work item = (kv head g, sequence b, split s) = cache rows
-// [s*split_rows, min((s+1)*split_rows, L_b)). The grid is (Hkv, B, splits):
-// the split index varies slowest, so the round-robin dispatch over the 8 XCDs
-// spreads every split index evenly over them (a split-fastest order would
-// pin split s to XCD s % 8 and, with ragged lengths, load the low XCDs far
-// more than the high ones), and splits that hold no rows are dispatched last
-// and exit at once.
+// [s*split_rows, min((s+1)*split_rows, L_b)). The grid is (Hkv, B, splits),
+// dispatched x fastest. With one length for the whole batch the split index
+// varies slowest: the round-robin dispatch over the 8 XCDs spreads every
+// split index evenly over them, the short last splits come last and splits
+// that hold no rows exit at once. With per-sequence lengths (up to
+// kReorderMaxB sequences) the dispatch order is remapped on the device: the
+// full splits of all sequences first, then the partial last splits, then
+// one unit per zero-length sequence (it writes the zero rows), then idle
+// workgroups. Full splits all cost the same, so the partial ones fill the
+// gaps at the end instead of a late full split running alone.
 //
 // bf16 (decode_bf16_kernel): each of the 4 waves walks its own tiles of BN
 // rows (BN*D*2 = 8 KiB of K and of V per tile) with non-temporal 16-byte
@@ -82,6 +86,66 @@ __device__ __forceinline__ Item make_item(const int32_t *seq_lens, int b,
   it.row1 = min(it.row0 + split_rows, it.L);
   it.n_split = (it.L + split_rows - 1) / split_rows;
   return it;
+}
+
+// ---------------------------------------------------------------------------
+// Work units
+// ---------------------------------------------------------------------------
+constexpr int kReorderMaxB = 256;
+
+struct Unit {
+  int g, b, s;  // kv head, sequence (-1: no work), split
+};
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// The work unit of this workgroup (the orders are described at the top).
+__device__ __forceinline__ Unit locate_unit(const int32_t *seq_lens, int B,
+                                            int Hkv, int max_length,
+                                            int split_rows) {
+  Unit u{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+  if (seq_lens == nullptr || B > kReorderMaxB) return u;
+  const int i = blockIdx.x + Hkv * (blockIdx.y + B * blockIdx.z);
+  u.g = i % Hkv;
+  int r = i / Hkv;  // rank among the (sequence, split) units; wave-uniform
+  const int lane = threadIdx.x % 64;
+  int Ls[kReorderMaxB / 64];
+#pragma unroll
+  for (int c = 0; c < kReorderMaxB / 64; ++c) {
+    const int bi = 64 * c + lane;
+    int L = bi < B ? seq_lens[bi] : 0;
+    Ls[c] = L < 0 ? 0 : (L > max_length ? max_length : L);
+  }
+  for (int cat = 0; cat < 3; ++cat) {  // full splits, partial splits, zero rows
+#pragma unroll
+    for (int c = 0; c < kReorderMaxB / 64; ++c) {
+      if (64 * c >= B) break;
+      const int L = Ls[c];
+      const int cnt = cat == 0   ? L / split_rows
+                      : cat == 1 ? (L % split_rows != 0)
+                                 : (64 * c + lane < B && L == 0);
+      const int incl = wave_incl_scan(cnt, lane);
+      const int tot = __shfl(incl, 63);
+      if (r < tot) {
+        const int ln = __ffsll((unsigned long long)__ballot(incl > r)) - 1;
+        u.b = 64 * c + ln;
+        const int excl = __shfl(incl - cnt, ln);
+        const int Lb = __shfl(L, ln);
+        u.s = cat == 0 ? r - excl : cat == 1 ? Lb / split_rows : 0;
+        return u;
+      }
+      r -= tot;
+    }
+  }
+  u.b = -1;
+  return u;
 }
 
 template <bool BF16>
@@ -163,9 +227,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
   __shared__ float fin_m[G], fin_l[G];
 
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
-  const int s = blockIdx.z;
+  const Unit un = locate_unit(seq_lens, gridDim.y, Hkv, max_length, split_rows);
+  if (un.b < 0) return;
+  const int g = un.g, b = un.b, s = un.s;
   const Item it = make_item(seq_lens, b, position_id, max_length, split_rows, s);
   if (it.row0 >= it.L) {
     if (it.L == 0 && s == 0) write_zero_rows<true, D, G, kThreads>(outp, b, g, Hq);
@@ -374,9 +438,9 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(
   __shared__ float sm_o[G * D];
   __shared__ float fin_m[G], fin_l[G];
 
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
-  const int s = blockIdx.z;
+  const Unit un = locate_unit(seq_lens, gridDim.y, Hkv, max_length, split_rows);
+  if (un.b < 0) return;
+  const int g = un.g, b = un.b, s = un.s;
   const Item it = make_item(seq_lens, b, position_id, max_length, split_rows, s);
   if (it.row0 >= it.L) {
     if (it.L == 0 && s == 0) write_zero_rows<false, D, G, kThreads>(outp, b, g, Hq);
