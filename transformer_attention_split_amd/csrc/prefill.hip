@@ -53,6 +53,8 @@ constexpr int NQG = 2;   // query groups per workgroup
 constexpr int kThreads = 512;
 constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag
+// buffer resource word 3 for raw (untyped, stride 0) 32-bit accesses
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   return __builtin_bit_cast(bf16x8_t, v);
@@ -379,6 +381,320 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// D = 64: one wave per key quarter, all 64 queries of the workgroup per wave
+// ---------------------------------------------------------------------------
+// Every matrix-core operand that is not a query has to cross the L1 path
+// (TA -> TCP) once per wave that uses it, and that path, not the matrix
+// cores, bounds a kernel whose waves share K and V tiles. Here a workgroup
+// of 4 waves takes 64 queries and wave w walks the 64-key tiles t with
+// t % 4 == w for all 64 queries (4 column blocks of 16): every K and V byte
+// of the head is read once per workgroup and every K or V operand feeds 4
+// products. One wave per SIMD; no barrier inside the key loop.
+//   * V tiles are staged per wave in its own LDS (two 8 KiB buffers) with
+//     buffer loads that write LDS directly. A tile is 64 rows of 128 bytes,
+//     unpadded; the 16-byte chunk c of row r sits at position
+//     c ^ 2*((r >> 1) & 3), so the 16 rows x 32 bytes of one transposing
+//     read spread over the banks;
+//   * K (straight into A-operand registers) and V are read through buffer
+//     resources limited to the rows [0, prefix + Lq): rows past the end read
+//     as zeros, and per-tile offsets are scalar. Both run two tiles ahead
+//     (two K register sets, two V buffers);
+//   * the running max is reduced across the four lanes of a query with
+//     v_permlane16_swap / v_permlane32_swap.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+struct P64 {
+  static constexpr int D = 64, NB = 4, NQW = 16 * NB, BM = NQW;
+  static constexpr int WAVES = NKQ, THREADS = 64 * WAVES;
+  static constexpr int KS = D / 32, NDB = D / 16, NKB = BN / 16;
+  static constexpr int ROWB = D * 2;            // bytes per cache row
+  static constexpr int VT_BYTES = BN * ROWB;    // one V tile: 8 KiB
+  static constexpr int NVBUF = 2;               // V buffers per wave
+  static constexpr int DMA = VT_BYTES / 1024;   // 1 KiB LDS loads per tile
+  static constexpr int LDS_V = WAVES * NVBUF * VT_BYTES;
+  static constexpr int LDS_MERGE = (NKQ * NQW * D + 2 * NKQ * NQW) * 4;
+  static constexpr int LDS = LDS_V > LDS_MERGE ? LDS_V : LDS_MERGE;
+};
+
+__device__ __forceinline__ float quad_max(float m) {
+  // max over lanes l, l ^ 16, l ^ 32, l ^ 48
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
+    const uint16_t *__restrict__ qg, const uint16_t *__restrict__ kg,
+    const uint16_t *__restrict__ vg, uint16_t *__restrict__ outg, int NH,
+    int Hq, int Hkv, int max_length, int Lq, int prefix, float qk_scale,
+    int n_qtiles, int heads_per_xcd) {
+  using T = P64;
+  constexpr int D = T::D, KS = T::KS, NDB = T::NDB, NKB = T::NKB;
+  constexpr int NB = T::NB, BM = T::BM, ROWB = T::ROWB;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  // ---- work item: (head instance, query tile) -----------------------------------
+  const int id = blockIdx.x;
+  const int xcd = id % kXcds;
+  const int k = id / kXcds;
+  const int j = xcd + kXcds * (k % heads_per_xcd);  // head instance b*Hq + h
+  if (j >= NH) return;
+  const int qt = __builtin_amdgcn_readfirstlane(n_qtiles - 1 - k / heads_per_xcd);
+  // (integer division runs on the vector ALUs; readfirstlane keeps the
+  // workgroup-uniform results in scalar registers)
+  const int b = __builtin_amdgcn_readfirstlane(j / Hq);
+  const int h = j % Hq;
+  const int kvh = __builtin_amdgcn_readfirstlane(h / (Hq / Hkv));
+
+  const int tid = threadIdx.x;
+  const int kq = __builtin_amdgcn_readfirstlane(tid / 64);  // key quarter = wave
+  const int l = tid % 64;
+  const int li = l % 16;
+  const int lg = l / 16;
+
+  const int kv_len = prefix + Lq;
+  const int q0 = qt * BM;                              // first query
+  const int kmax = prefix + min(q0 + BM - 1, Lq - 1);  // last visible key
+  const int last_tile = kmax / BN;
+  // this wave's tiles: t_n = kq + 4 n, n < nt
+  const int nt = kq <= last_tile ? (last_tile - kq) / NKQ + 1 : 0;
+
+  const size_t kvbase = ((size_t)b * Hkv + kvh) * (size_t)max_length * D;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(kg + kvbase), (short)0, kv_len * ROWB, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(vg + kvbase), (short)0, kv_len * ROWB, kBufferFlags);
+
+  // The queries as B operands (column li of block nb).
+  bf16x8_t qf[NB][KS];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int qme = q0 + nb * 16 + li;
+    const size_t qrow = ((size_t)j * Lq + (size_t)qme) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (qme < Lq) v = *reinterpret_cast<const u32x4_t *>(qg + qrow + ks * 32 + 8 * lg);
+      qf[nb][ks] = as_bf16x8(v);
+    }
+  }
+  const u32x4_t ones_w = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  const bf16x8_t ones = as_bf16x8(ones_w);
+
+  f32x4_t o[NB][NDB];
+  f32x4_t lacc[NB];
+  float mc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) o[nb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    lacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    mc[nb] = kNegInf;
+  }
+
+  // K: lane (li, lg) of block kb loads row 16 kb + li, bytes 64 ks + 16 lg.
+  const int koff = li * ROWB + lg * 16;
+  auto load_k = [&](int t, u32x4_t (&kr)[NKB][KS]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kr[kb][ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+            krs, koff + ks * 64, t * T::VT_BYTES + kb * 16 * ROWB, 0));
+  };
+  // V: load jj of a tile fills LDS bytes [1024 jj, 1024 jj + 1024) of the
+  // buffer; lane l writes position l % 8 of row 8 jj + l / 8 and therefore
+  // reads chunk (l % 8) ^ 2 lg of that row.
+  const int voff = (l / 8) * ROWB + ((l % 8) ^ (2 * lg)) * 16;
+  unsigned char *vlds = smem + (size_t)kq * T::NVBUF * T::VT_BYTES;
+  auto issue_v = [&](int t, int buf) {
+#pragma unroll
+    for (int jj = 0; jj < T::DMA; ++jj)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, (lds_void_t *)(vlds + buf * T::VT_BYTES + jj * 1024), 16, voff,
+          t * T::VT_BYTES + jj * 1024, 0, 0);
+  };
+  // Transposing reads: lane (li, lg) names row 4 lg + li / 4 (+ 32 t2, + 16)
+  // and the 8 bytes of chunk 2 db + (li >> 1) % 2, half li % 2, of that row.
+  int tro[NDB];
+  {
+    const int fh = (2 * lg + (li >> 3)) & 3;
+    const int base = (4 * lg + (li >> 2)) * ROWB + ((li >> 1) & 1) * 16 + (li & 1) * 8;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) tro[db] = base + 32 * (db ^ fh);
+  }
+
+  auto step = [&](int n, u32x4_t (&kc)[NKB][KS]) {
+    const int t = kq + NKQ * n;
+    const int j0 = t * BN;
+    const int buf = n & 1;
+    // ---- Sᵀ = K·Qᵀ (raw scores), every K operand feeds NB query blocks ----------
+    f32x4_t s[NB][NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[nb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t a = as_bf16x8(kc[kb][ks]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          s[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[nb][kb], 0, 0, 0);
+      }
+    }
+    // ---- softmax of this tile ----------------------------------------------------
+    bf16x8_t pb[NB][BN / 32];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if (j0 + BN - 1 > prefix + q0 + nb * 16) [[unlikely]] {
+        // key j0 + 16 kb + 4 lg + r is visible iff 16 kb + r <= lim
+        const int lim = prefix + q0 + nb * 16 + li - j0 - 4 * lg;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kb + r > lim) s[nb][kb][r] = kNegInf;
+      }
+      float m0 = max3(s[nb][0][0], s[nb][0][1], s[nb][0][2]);
+      m0 = max3(m0, s[nb][0][3], s[nb][1][0]);
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb) {
+        m0 = max3(m0, s[nb][kb][1], s[nb][kb][2]);
+        m0 = kb + 1 < NKB ? max3(m0, s[nb][kb][3], s[nb][kb + 1][0])
+                          : fmaxf(m0, s[nb][kb][3]);
+      }
+      m0 = quad_max(m0);
+      const float mloc_c = m0 * qk_scale;
+      if (__any(mloc_c > mc[nb] + kRescaleSlack)) [[unlikely]] {
+        const float mnew = fmaxf(mc[nb], mloc_c);
+        // a query with no visible key yet keeps max -inf: no rescale (and
+        // no -inf - -inf)
+        const float alpha = mnew == mc[nb] ? 1.f : fast_exp2(mc[nb] - mnew);
+        mc[nb] = mnew;
+        lacc[nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[nb][db] *= alpha;
+      }
+      // every score of a query with max -inf is masked: any finite offset
+      // gives p = 0 (and -mc would be +inf)
+      const float nmc = mc[nb] == kNegInf ? 0.f : -mc[nb];
+#pragma unroll
+      for (int t2 = 0; t2 < BN / 32; ++t2) {
+        float p[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = fast_exp2(fmaf(s[nb][2 * t2][r], qk_scale, nmc));
+          p[4 + r] = fast_exp2(fmaf(s[nb][2 * t2 + 1][r], qk_scale, nmc));
+        }
+        const u32x4_t pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        pb[nb][t2] = as_bf16x8(pw);
+      }
+    }
+    // ---- row sums and Oᵀ += Vᵀ·Pᵀ, every V operand feeds NB query blocks ---------
+    const unsigned char *vt = vlds + buf * T::VT_BYTES;
+#pragma unroll
+    for (int t2 = 0; t2 < BN / 32; ++t2) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        lacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[nb][t2], lacc[nb], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(vt + tro[db] + t2 * 32 * ROWB);
+        const u32x2_t lo = read_tr16(src);
+        const u32x2_t hi = read_tr16(src + 16 * ROWB / 2);
+        const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
+        const bf16x8_t a = as_bf16x8(av);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nb][t2], o[nb][db], 0, 0, 0);
+      }
+    }
+    // ---- V and K two tiles ahead (V into the buffer just read, K into the
+    // registers this tile used). V goes first: memory operations complete in
+    // order, so the next wait for K does not also wait for these V loads.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the reads above are done
+    issue_v(t + 2 * NKQ, buf);
+    load_k(t + 2 * NKQ, kc);
+  };
+
+  // K and V run two tiles ahead: two K register sets and two V buffers.
+  u32x4_t ka[NKB][KS], kb2[NKB][KS];
+  issue_v(kq, 0);
+  load_k(kq, ka);
+  issue_v(kq + NKQ, 1);
+  load_k(kq + NKQ, kb2);
+  int n = 0;
+  for (; n + 1 < nt; n += 2) {
+    step(n, ka);
+    step(n + 1, kb2);
+  }
+  if (n < nt) step(n, ka);
+  __syncthreads();  // every wave is done with its V buffers
+
+  // ---- merge the key quarters (log-sum-exp), store --------------------------------
+  float *mo = reinterpret_cast<float *>(smem);  // [NKQ][BM][D]
+  float *mm = mo + NKQ * BM * D;                // [NKQ][BM]
+  float *ml = mm + NKQ * BM;                    // [NKQ][BM]
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int qi = nb * 16 + li;  // query inside the tile
+    float *dst = mo + ((size_t)kq * BM + qi) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4_t *>(dst + db * 16 + 4 * lg) = o[nb][db];
+    if (lg == 0) {
+      mm[kq * BM + qi] = mc[nb];
+      ml[kq * BM + qi] = lacc[nb][0];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < BM * D / 2; i += T::THREADS) {
+    const int q = (2 * i) / D;  // query inside the tile
+    const int d = (2 * i) % D;  // even dimension; this thread does d, d+1
+    const int qglob = q0 + q;
+    if (qglob >= Lq) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int kk = 0; kk < NKQ; ++kk) M = fmaxf(M, mm[kk * BM + q]);
+    float a0 = 0.f, a1 = 0.f, lt = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKQ; ++kk) {
+      const float mk = mm[kk * BM + q];
+      // a key quarter that saw no key of this query contributes nothing
+      const float wgt = mk == kNegInf ? 0.f : fast_exp2(mk - M);
+      const float *src = mo + ((size_t)kk * BM + q) * D + d;
+      a0 = fmaf(wgt, src[0], a0);
+      a1 = fmaf(wgt, src[1], a1);
+      lt = fmaf(wgt, ml[kk * BM + q], lt);
+    }
+    const float inv = 1.f / lt;
+    *reinterpret_cast<uint32_t *>(outg + ((size_t)j * Lq + qglob) * D + d) =
+        pack_bf16x2(a0 * inv, a1 * inv);
+  }
+}
+
+hipError_t launch_64(const PrefillArgs &a, hipStream_t stream) {
+  using T = P64;
+  const int n_qtiles = (a.Lq + T::BM - 1) / T::BM;
+  const int NH = a.B * a.Hq;
+  const int heads_per_xcd = (NH + kXcds - 1) / kXcds;
+  const long blocks = (long)kXcds * heads_per_xcd * n_qtiles;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&prefill64_kernel),
+      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+  if (e != hipSuccess) return e;
+  prefill64_kernel<<<dim3((unsigned)blocks), T::THREADS, T::LDS, stream>>>(
+      static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
+      static_cast<const uint16_t *>(a.v), static_cast<uint16_t *>(a.out), NH,
+      a.Hq, a.Hkv, a.max_length, a.Lq, a.prefix_len, a.scale * kLog2e,
+      n_qtiles, heads_per_xcd);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
   using T = Tile<D>;
@@ -404,7 +720,7 @@ hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
-  return a.D == 64 ? launch_d<64>(a, stream) : launch_d<128>(a, stream);
+  return a.D == 64 ? launch_64(a, stream) : launch_d<128>(a, stream);
 }
 
 }  // namespace attn
