@@ -410,11 +410,8 @@ struct P64 {
   static constexpr int KS = D / 32, NDB = D / 16, NKB = BN / 16;
   static constexpr int ROWB = D * 2;            // bytes per cache row
   static constexpr int VT_BYTES = BN * ROWB;    // one V tile: 8 KiB
-  static constexpr int NVBUF = 2;               // V buffers per wave
   static constexpr int DMA = VT_BYTES / 1024;   // 1 KiB LDS loads per tile
-  static constexpr int LDS_V = WAVES * NVBUF * VT_BYTES;
-  static constexpr int LDS_MERGE = (NKQ * NQW * D + 2 * NKQ * NQW) * 4;
-  static constexpr int LDS = LDS_V > LDS_MERGE ? LDS_V : LDS_MERGE;
+  static constexpr int VBUF = WAVES * VT_BYTES; // one buffer of every wave
 };
 
 __device__ __forceinline__ float quad_max(float m) {
@@ -433,7 +430,10 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
   using T = P64;
   constexpr int D = T::D, KS = T::KS, NDB = T::NDB, NKB = T::NKB;
   constexpr int NB = T::NB, BM = T::BM, ROWB = T::ROWB;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // Three V buffers as separate LDS objects: the compiler can then tell a
+  // direct load into one buffer from reads of another and does not make the
+  // reads wait for it.
+  __shared__ __attribute__((aligned(16))) unsigned char vb0[T::VBUF], vb1[T::VBUF], vb2[T::VBUF];
 
   // ---- work item: (head instance, query tile) -----------------------------------
   const int id = blockIdx.x;
@@ -508,12 +508,12 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
   // buffer; lane l writes position l % 8 of row 8 jj + l / 8 and therefore
   // reads chunk (l % 8) ^ 2 lg of that row.
   const int voff = (l / 8) * ROWB + ((l % 8) ^ (2 * lg)) * 16;
-  unsigned char *vlds = smem + (size_t)kq * T::NVBUF * T::VT_BYTES;
-  auto issue_v = [&](int t, int buf) {
+  const int vwave = kq * T::VT_BYTES;  // this wave's tile inside a buffer
+  auto issue_v = [&](int t, unsigned char *buf) {
 #pragma unroll
     for (int jj = 0; jj < T::DMA; ++jj)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vrs, (lds_void_t *)(vlds + buf * T::VT_BYTES + jj * 1024), 16, voff,
+          vrs, (lds_void_t *)(buf + vwave + jj * 1024), 16, voff,
           t * T::VT_BYTES + jj * 1024, 0, 0);
   };
   // Transposing reads: lane (li, lg) names row 4 lg + li / 4 (+ 32 t2, + 16)
@@ -526,10 +526,14 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
     for (int db = 0; db < NDB; ++db) tro[db] = base + 32 * (db ^ fh);
   }
 
-  auto step = [&](int n, u32x4_t (&kc)[NKB][KS]) {
+  // Step n (tile t): the scores go to the matrix cores, then V of tile t+8
+  // is loaded into `vnext` (last read two steps ago) and K of tile t+4 into
+  // the K registers (once the products above have read them); V of tile t
+  // is read from `vcur`.
+  u32x4_t kc[NKB][KS];
+  auto step = [&](int n, const unsigned char *vcur, unsigned char *vnext) {
     const int t = kq + NKQ * n;
     const int j0 = t * BN;
-    const int buf = n & 1;
     // ---- Sᵀ = K·Qᵀ (raw scores), every K operand feeds NB query blocks ----------
     f32x4_t s[NB][NKB];
 #pragma unroll
@@ -544,6 +548,9 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
           s[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[nb][kb], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): older reads of vnext done
+    issue_v(t + 2 * NKQ, vnext);
+    load_k(t + NKQ, kc);
     // ---- softmax of this tile ----------------------------------------------------
     bf16x8_t pb[NB][BN / 32];
 #pragma unroll
@@ -594,7 +601,7 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
       }
     }
     // ---- row sums and Oᵀ += Vᵀ·Pᵀ, every V operand feeds NB query blocks ---------
-    const unsigned char *vt = vlds + buf * T::VT_BYTES;
+    const unsigned char *vt = vcur + vwave;
 #pragma unroll
     for (int t2 = 0; t2 < BN / 32; ++t2) {
 #pragma unroll
@@ -612,42 +619,42 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
           o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nb][t2], o[nb][db], 0, 0, 0);
       }
     }
-    // ---- V and K two tiles ahead (V into the buffer just read, K into the
-    // registers this tile used). V goes first: memory operations complete in
-    // order, so the next wait for K does not also wait for these V loads.
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the reads above are done
-    issue_v(t + 2 * NKQ, buf);
-    load_k(t + 2 * NKQ, kc);
   };
 
-  // K and V run two tiles ahead: two K register sets and two V buffers.
-  u32x4_t ka[NKB][KS], kb2[NKB][KS];
-  issue_v(kq, 0);
-  load_k(kq, ka);
-  issue_v(kq + NKQ, 1);
-  load_k(kq + NKQ, kb2);
+  issue_v(kq, vb0);
+  issue_v(kq + NKQ, vb1);
+  load_k(kq, kc);
   int n = 0;
-  for (; n + 1 < nt; n += 2) {
-    step(n, ka);
-    step(n + 1, kb2);
+  for (; n + 2 < nt; n += 3) {
+    step(n, vb0, vb2);
+    step(n + 1, vb1, vb0);
+    step(n + 2, vb2, vb1);
   }
-  if (n < nt) step(n, ka);
-  __syncthreads();  // every wave is done with its V buffers
+  if (n < nt) step(n, vb0, vb2);
+  if (n + 1 < nt) step(n + 1, vb1, vb0);
+  __builtin_amdgcn_s_waitcnt(0);  // no direct LDS load may still be in flight
+  __syncthreads();                // every wave is done with its V buffers
 
   // ---- merge the key quarters (log-sum-exp), store --------------------------------
-  float *mo = reinterpret_cast<float *>(smem);  // [NKQ][BM][D]
-  float *mm = mo + NKQ * BM * D;                // [NKQ][BM]
-  float *ml = mm + NKQ * BM;                    // [NKQ][BM]
+  // quarter kk's [BM][D] outputs: 16 KiB in vb0 (kk = 0, 1) or vb1 (kk = 2, 3);
+  // running max and sum [NKQ][BM] in vb2
+  auto mo_of = [&](int kk) {
+    return reinterpret_cast<float *>((kk < 2 ? vb0 : vb1) + (kk & 1) * BM * D * 4);
+  };
+  float *mm = reinterpret_cast<float *>(vb2);  // [NKQ][BM]
+  float *ml = mm + NKQ * BM;                   // [NKQ][BM]
+  {
+    float *mo = mo_of(kq);
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int qi = nb * 16 + li;  // query inside the tile
-    float *dst = mo + ((size_t)kq * BM + qi) * D;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int qi = nb * 16 + li;  // query inside the tile
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<f32x4_t *>(dst + db * 16 + 4 * lg) = o[nb][db];
-    if (lg == 0) {
-      mm[kq * BM + qi] = mc[nb];
-      ml[kq * BM + qi] = lacc[nb][0];
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4_t *>(mo + qi * D + db * 16 + 4 * lg) = o[nb][db];
+      if (lg == 0) {
+        mm[kq * BM + qi] = mc[nb];
+        ml[kq * BM + qi] = lacc[nb][0];
+      }
     }
   }
   __syncthreads();
@@ -665,7 +672,7 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
       const float mk = mm[kk * BM + q];
       // a key quarter that saw no key of this query contributes nothing
       const float wgt = mk == kNegInf ? 0.f : fast_exp2(mk - M);
-      const float *src = mo + ((size_t)kk * BM + q) * D + d;
+      const float *src = mo_of(kk) + q * D + d;
       a0 = fmaf(wgt, src[0], a0);
       a1 = fmaf(wgt, src[1], a1);
       lt = fmaf(wgt, ml[kk * BM + q], lt);
@@ -683,11 +690,7 @@ hipError_t launch_64(const PrefillArgs &a, hipStream_t stream) {
   const int heads_per_xcd = (NH + kXcds - 1) / kXcds;
   const long blocks = (long)kXcds * heads_per_xcd * n_qtiles;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&prefill64_kernel),
-      hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
-  if (e != hipSuccess) return e;
-  prefill64_kernel<<<dim3((unsigned)blocks), T::THREADS, T::LDS, stream>>>(
+  prefill64_kernel<<<dim3((unsigned)blocks), T::THREADS, 0, stream>>>(
       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
       static_cast<const uint16_t *>(a.v), static_cast<uint16_t *>(a.out), NH,
       a.Hq, a.Hkv, a.max_length, a.Lq, a.prefix_len, a.scale * kLog2e,
