@@ -382,36 +382,35 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// D = 64: one wave per key quarter, all 64 queries of the workgroup per wave
+// D = 64: K and V staged once per workgroup in LDS
 // ---------------------------------------------------------------------------
-// Every matrix-core operand that is not a query has to cross the L1 path
-// (TA -> TCP) once per wave that uses it, and that path, not the matrix
-// cores, bounds a kernel whose waves share K and V tiles. Here a workgroup
-// of 4 waves takes 64 queries and wave w walks the 64-key tiles t with
-// t % 4 == w for all 64 queries (4 column blocks of 16): every K and V byte
-// of the head is read once per workgroup and every K or V operand feeds 4
-// products. One wave per SIMD; no barrier inside the key loop.
-//   * V tiles are staged per wave in its own LDS (two 8 KiB buffers) with
-//     buffer loads that write LDS directly. A tile is 64 rows of 128 bytes,
-//     unpadded; the 16-byte chunk c of row r sits at position
-//     c ^ 2*((r >> 1) & 3), so the 16 rows x 32 bytes of one transposing
-//     read spread over the banks;
-//   * K (straight into A-operand registers) and V are read through buffer
-//     resources limited to the rows [0, prefix + Lq): rows past the end read
-//     as zeros, and per-tile offsets are scalar. Both run two tiles ahead
-//     (two K register sets, two V buffers);
-//   * the running max is reduced across the four lanes of a query with
+// A workgroup of 8 waves takes 64 queries: query group qg = w / 4 (32
+// queries, 2 column blocks of 16) x key quarter kq = w % 4 (tiles t with
+// t % 4 == kq). Two waves per SIMD hide each other's latencies.
+//   * Every 64-key tile of K and of V crosses the L1 path once per
+//     workgroup: iteration it's four K tiles and four V tiles are loaded with
+//     buffer loads that write LDS directly (wave (0, kq) loads K tile kq,
+//     wave (1, kq) loads V tile kq), double-buffered, one workgroup barrier
+//     per iteration. The next iteration's loads are issued before this
+//     iteration is computed.
+//   * LDS tiles are 64 rows of 128 bytes, unpadded, with the 16-byte chunk c
+//     of row r at position c ^ ((r >> 1) & 7) for K (the 16 rows x 16 bytes
+//     of one A-operand read fall on distinct banks) and c ^ 2*((r >> 1) & 3)
+//     for V (likewise for the 16 rows x 32 bytes of one transposing read).
+//   * K and V are read through buffer resources limited to the rows
+//     [0, prefix + Lq): rows past the end read as zeros.
+//   * The running max is reduced across the four lanes of a query with
 //     v_permlane16_swap / v_permlane32_swap.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 struct P64 {
-  static constexpr int D = 64, NB = 4, NQW = 16 * NB, BM = NQW;
-  static constexpr int WAVES = NKQ, THREADS = 64 * WAVES;
+  static constexpr int D = 64, NB = 2, NQW = 16 * NB, BM = NQG * NQW;
+  static constexpr int THREADS = 64 * NQG * NKQ;
   static constexpr int KS = D / 32, NDB = D / 16, NKB = BN / 16;
-  static constexpr int ROWB = D * 2;            // bytes per cache row
-  static constexpr int VT_BYTES = BN * ROWB;    // one V tile: 8 KiB
-  static constexpr int DMA = VT_BYTES / 1024;   // 1 KiB LDS loads per tile
-  static constexpr int VBUF = WAVES * VT_BYTES; // one buffer of every wave
+  static constexpr int ROWB = D * 2;             // bytes per cache row
+  static constexpr int T_BYTES = BN * ROWB;      // one tile: 8 KiB
+  static constexpr int DMA = T_BYTES / 1024;     // 1 KiB LDS loads per tile
+  static constexpr int BUF = NKQ * T_BYTES;      // one iteration of K (or V)
 };
 
 __device__ __forceinline__ float quad_max(float m) {
@@ -429,11 +428,12 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
     int n_qtiles, int heads_per_xcd) {
   using T = P64;
   constexpr int D = T::D, KS = T::KS, NDB = T::NDB, NKB = T::NKB;
-  constexpr int NB = T::NB, BM = T::BM, ROWB = T::ROWB;
-  // Three V buffers as separate LDS objects: the compiler can then tell a
-  // direct load into one buffer from reads of another and does not make the
-  // reads wait for it.
-  __shared__ __attribute__((aligned(16))) unsigned char vb0[T::VBUF], vb1[T::VBUF], vb2[T::VBUF];
+  constexpr int NB = T::NB, NQW = T::NQW, BM = T::BM, ROWB = T::ROWB;
+  // K and V buffers of the two iterations in flight, as separate LDS
+  // objects: the compiler then tells a direct load into one from reads of
+  // another and does not make the reads wait for it.
+  __shared__ __attribute__((aligned(16))) unsigned char kb0[T::BUF], kb1[T::BUF],
+      vb0[T::BUF], vb1[T::BUF];
 
   // ---- work item: (head instance, query tile) -----------------------------------
   const int id = blockIdx.x;
@@ -441,37 +441,40 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
   const int k = id / kXcds;
   const int j = xcd + kXcds * (k % heads_per_xcd);  // head instance b*Hq + h
   if (j >= NH) return;
-  const int qt = __builtin_amdgcn_readfirstlane(n_qtiles - 1 - k / heads_per_xcd);
   // (integer division runs on the vector ALUs; readfirstlane keeps the
   // workgroup-uniform results in scalar registers)
+  const int qt = __builtin_amdgcn_readfirstlane(n_qtiles - 1 - k / heads_per_xcd);
   const int b = __builtin_amdgcn_readfirstlane(j / Hq);
   const int h = j % Hq;
   const int kvh = __builtin_amdgcn_readfirstlane(h / (Hq / Hkv));
 
   const int tid = threadIdx.x;
-  const int kq = __builtin_amdgcn_readfirstlane(tid / 64);  // key quarter = wave
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int l = tid % 64;
   const int li = l % 16;
   const int lg = l / 16;
+  const int kq = w % NKQ;   // key quarter
+  const int qgi = w / NKQ;  // query group
 
   const int kv_len = prefix + Lq;
-  const int q0 = qt * BM;                              // first query
-  const int kmax = prefix + min(q0 + BM - 1, Lq - 1);  // last visible key
-  const int last_tile = kmax / BN;
-  // this wave's tiles: t_n = kq + 4 n, n < nt
-  const int nt = kq <= last_tile ? (last_tile - kq) / NKQ + 1 : 0;
+  const int q_end = min((qt + 1) * BM, Lq);
+  const int n_tiles = (prefix + q_end + BN - 1) / BN;  // tiles the workgroup sees
+  const int n_iter = (n_tiles + NKQ - 1) / NKQ;
+  const int qg0 = qt * BM + qgi * NQW;  // first query of this wave's group
+  const bool g_active = qg0 < Lq;
+  const int g_kmax = prefix + min(qg0 + NQW - 1, Lq - 1);  // last visible key
 
   const size_t kvbase = ((size_t)b * Hkv + kvh) * (size_t)max_length * D;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(kg + kvbase), (short)0, kv_len * ROWB, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>(vg + kvbase), (short)0, kv_len * ROWB, kBufferFlags);
+  // wave (0, kq) streams K, wave (1, kq) streams V
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>((qgi == 0 ? kg : vg) + kvbase), (short)0, kv_len * ROWB,
+      kBufferFlags);
 
-  // The queries as B operands (column li of block nb).
+  // This wave's queries as B operands (column li of block nb).
   bf16x8_t qf[NB][KS];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int qme = q0 + nb * 16 + li;
+    const int qme = qg0 + nb * 16 + li;
     const size_t qrow = ((size_t)j * Lq + (size_t)qme) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -494,30 +497,33 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
     mc[nb] = kNegInf;
   }
 
-  // K: lane (li, lg) of block kb loads row 16 kb + li, bytes 64 ks + 16 lg.
-  const int koff = li * ROWB + lg * 16;
-  auto load_k = [&](int t, u32x4_t (&kr)[NKB][KS]) {
+  // Loads: load jj of a tile fills LDS bytes [1024 jj, 1024 jj + 1024); lane
+  // l writes position l % 8 of row 8 jj + l / 8 and reads the chunk that
+  // belongs there.
+  int dma_off[2];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kr[kb][ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-            krs, koff + ks * 64, t * T::VT_BYTES + kb * 16 * ROWB, 0));
-  };
-  // V: load jj of a tile fills LDS bytes [1024 jj, 1024 jj + 1024) of the
-  // buffer; lane l writes position l % 8 of row 8 jj + l / 8 and therefore
-  // reads chunk (l % 8) ^ 2 lg of that row.
-  const int voff = (l / 8) * ROWB + ((l % 8) ^ (2 * lg)) * 16;
-  const int vwave = kq * T::VT_BYTES;  // this wave's tile inside a buffer
-  auto issue_v = [&](int t, unsigned char *buf) {
+  for (int par = 0; par < 2; ++par) {
+    const int pos = l % 8;
+    const int chunk = qgi == 0 ? pos ^ ((4 * par + lg) & 7)  // K: c ^ ((r >> 1) & 7)
+                               : pos ^ (2 * lg);            // V: c ^ 2((r >> 1) & 3)
+    dma_off[par] = (l / 8) * ROWB + chunk * 16;
+  }
+  auto issue = [&](int it, unsigned char *kbuf, unsigned char *vbuf) {
+    unsigned char *dst = (qgi == 0 ? kbuf : vbuf) + kq * T::T_BYTES;
+    const int t = it * NKQ + kq;
 #pragma unroll
     for (int jj = 0; jj < T::DMA; ++jj)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          vrs, (lds_void_t *)(buf + vwave + jj * 1024), 16, voff,
-          t * T::VT_BYTES + jj * 1024, 0, 0);
+          rs, (lds_void_t *)(dst + jj * 1024), 16, dma_off[jj & 1],
+          t * T::T_BYTES + jj * 1024, 0, 0);
   };
-  // Transposing reads: lane (li, lg) names row 4 lg + li / 4 (+ 32 t2, + 16)
-  // and the 8 bytes of chunk 2 db + (li >> 1) % 2, half li % 2, of that row.
+  // A-operand reads of K: block kb, k-step ks -> row 16 kb + li, chunk
+  // 4 ks + lg at position (4 ks + lg) ^ (li >> 1).
+  int kro[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kro[ks] = li * ROWB + (((4 * ks + lg) ^ (li >> 1)) * 16);
+  // Transposing reads of V: lane (li, lg) names row 4 lg + li / 4 (+ 32 t2,
+  // + 16) and the 8 bytes of chunk 2 db + (li >> 1) % 2, half li % 2.
   int tro[NDB];
   {
     const int fh = (2 * lg + (li >> 3)) & 3;
@@ -526,14 +532,12 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
     for (int db = 0; db < NDB; ++db) tro[db] = base + 32 * (db ^ fh);
   }
 
-  // Step n (tile t): the scores go to the matrix cores, then V of tile t+8
-  // is loaded into `vnext` (last read two steps ago) and K of tile t+4 into
-  // the K registers (once the products above have read them); V of tile t
-  // is read from `vcur`.
-  u32x4_t kc[NKB][KS];
-  auto step = [&](int n, const unsigned char *vcur, unsigned char *vnext) {
-    const int t = kq + NKQ * n;
+  auto compute = [&](int it, const unsigned char *kbuf, const unsigned char *vbuf) {
+    const int t = it * NKQ + kq;
     const int j0 = t * BN;
+    if (!(t < n_tiles && g_active && j0 <= g_kmax)) return;
+    const unsigned char *kt = kbuf + kq * T::T_BYTES;
+    const unsigned char *vt = vbuf + kq * T::T_BYTES;
     // ---- Sᵀ = K·Qᵀ (raw scores), every K operand feeds NB query blocks ----------
     f32x4_t s[NB][NKB];
 #pragma unroll
@@ -542,28 +546,27 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
       for (int nb = 0; nb < NB; ++nb) s[nb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a = as_bf16x8(kc[kb][ks]);
+        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t *>(kt + kb * 16 * ROWB + kro[ks]));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           s[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[nb][kb], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): older reads of vnext done
-    issue_v(t + 2 * NKQ, vnext);
-    load_k(t + NKQ, kc);
-    // ---- softmax of this tile ----------------------------------------------------
+    const bool diag = j0 + BN - 1 > prefix + qg0;
     bf16x8_t pb[NB][BN / 32];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (j0 + BN - 1 > prefix + q0 + nb * 16) [[unlikely]] {
+      // ---- causal mask (diagonal tiles only) -----------------------------------
+      if (diag) [[unlikely]] {
         // key j0 + 16 kb + 4 lg + r is visible iff 16 kb + r <= lim
-        const int lim = prefix + q0 + nb * 16 + li - j0 - 4 * lg;
+        const int lim = prefix + qg0 + nb * 16 + li - j0 - 4 * lg;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (16 * kb + r > lim) s[nb][kb][r] = kNegInf;
       }
+      // ---- running max over the 4 lanes of the query; lazy rescale ---------
       float m0 = max3(s[nb][0][0], s[nb][0][1], s[nb][0][2]);
       m0 = max3(m0, s[nb][0][3], s[nb][1][0]);
 #pragma unroll
@@ -572,8 +575,7 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
         m0 = kb + 1 < NKB ? max3(m0, s[nb][kb][3], s[nb][kb + 1][0])
                           : fmaxf(m0, s[nb][kb][3]);
       }
-      m0 = quad_max(m0);
-      const float mloc_c = m0 * qk_scale;
+      const float mloc_c = quad_max(m0) * qk_scale;
       if (__any(mloc_c > mc[nb] + kRescaleSlack)) [[unlikely]] {
         const float mnew = fmaxf(mc[nb], mloc_c);
         // a query with no visible key yet keeps max -inf: no rescale (and
@@ -601,7 +603,6 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
       }
     }
     // ---- row sums and Oᵀ += Vᵀ·Pᵀ, every V operand feeds NB query blocks ---------
-    const unsigned char *vt = vcur + vwave;
 #pragma unroll
     for (int t2 = 0; t2 < BN / 32; ++t2) {
 #pragma unroll
@@ -620,62 +621,70 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
       }
     }
   };
-
-  issue_v(kq, vb0);
-  issue_v(kq + NKQ, vb1);
-  load_k(kq, kc);
-  int n = 0;
-  for (; n + 2 < nt; n += 3) {
-    step(n, vb0, vb2);
-    step(n + 1, vb1, vb0);
-    step(n + 2, vb2, vb1);
-  }
-  if (n < nt) step(n, vb0, vb2);
-  if (n + 1 < nt) step(n + 1, vb1, vb0);
-  __builtin_amdgcn_s_waitcnt(0);  // no direct LDS load may still be in flight
-  __syncthreads();                // every wave is done with its V buffers
-
-  // ---- merge the key quarters (log-sum-exp), store --------------------------------
-  // quarter kk's [BM][D] outputs: 16 KiB in vb0 (kk = 0, 1) or vb1 (kk = 2, 3);
-  // running max and sum [NKQ][BM] in vb2
-  auto mo_of = [&](int kk) {
-    return reinterpret_cast<float *>((kk < 2 ? vb0 : vb1) + (kk & 1) * BM * D * 4);
+  // the loads of an iteration are complete in every wave after this
+  auto sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
-  float *mm = reinterpret_cast<float *>(vb2);  // [NKQ][BM]
-  float *ml = mm + NKQ * BM;                   // [NKQ][BM]
+
+  issue(0, kb0, vb0);
+  sync();
+  int it = 0;
+  for (; it + 1 < n_iter; it += 2) {
+    issue(it + 1, kb1, vb1);
+    compute(it, kb0, vb0);
+    sync();
+    issue(it + 2, kb0, vb0);
+    compute(it + 1, kb1, vb1);
+    sync();
+  }
+  if (it < n_iter) {
+    compute(it, kb0, vb0);
+    sync();
+  }
+
+  // ---- merge the key quarters of each query group (log-sum-exp), store -----------
+  // outputs [NQG][NKQ][NQW][D] in kb0 (group 0) and kb1 (group 1); running
+  // max and sum [NQG][NKQ][NQW] in vb0
+  auto mo_of = [&](int grp, int kk) {
+    return reinterpret_cast<float *>((grp == 0 ? kb0 : kb1) + kk * NQW * D * 4);
+  };
+  float *mm = reinterpret_cast<float *>(vb0);  // [NQG][NKQ][NQW]
+  float *ml = mm + NQG * NKQ * NQW;            // [NQG][NKQ][NQW]
   {
-    float *mo = mo_of(kq);
+    float *mo = mo_of(qgi, kq);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int qi = nb * 16 + li;  // query inside the tile
+      const int qi = nb * 16 + li;  // query inside the group
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         *reinterpret_cast<f32x4_t *>(mo + qi * D + db * 16 + 4 * lg) = o[nb][db];
       if (lg == 0) {
-        mm[kq * BM + qi] = mc[nb];
-        ml[kq * BM + qi] = lacc[nb][0];
+        mm[(qgi * NKQ + kq) * NQW + qi] = mc[nb];
+        ml[(qgi * NKQ + kq) * NQW + qi] = lacc[nb][0];
       }
     }
   }
   __syncthreads();
   for (int i = tid; i < BM * D / 2; i += T::THREADS) {
-    const int q = (2 * i) / D;  // query inside the tile
-    const int d = (2 * i) % D;  // even dimension; this thread does d, d+1
-    const int qglob = q0 + q;
+    const int q = (2 * i) / D;       // query inside the workgroup
+    const int d = (2 * i) % D;       // even dimension; this thread does d, d+1
+    const int grp = q / NQW, qi = q % NQW;
+    const int qglob = qt * BM + q;
     if (qglob >= Lq) continue;
     float M = kNegInf;
 #pragma unroll
-    for (int kk = 0; kk < NKQ; ++kk) M = fmaxf(M, mm[kk * BM + q]);
+    for (int kk = 0; kk < NKQ; ++kk) M = fmaxf(M, mm[(grp * NKQ + kk) * NQW + qi]);
     float a0 = 0.f, a1 = 0.f, lt = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NKQ; ++kk) {
-      const float mk = mm[kk * BM + q];
+      const float mk = mm[(grp * NKQ + kk) * NQW + qi];
       // a key quarter that saw no key of this query contributes nothing
       const float wgt = mk == kNegInf ? 0.f : fast_exp2(mk - M);
-      const float *src = mo_of(kk) + q * D + d;
+      const float *src = mo_of(grp, kk) + qi * D + d;
       a0 = fmaf(wgt, src[0], a0);
       a1 = fmaf(wgt, src[1], a1);
-      lt = fmaf(wgt, ml[kk * BM + q], lt);
+      lt = fmaf(wgt, ml[(grp * NKQ + kk) * NQW + qi], lt);
     }
     const float inv = 1.f / lt;
     *reinterpret_cast<uint32_t *>(outg + ((size_t)j * Lq + qglob) * D + d) =
