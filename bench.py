@@ -316,10 +316,10 @@ def main():
         secondary["decode_single_pos8000"] = bench_single_position(
             torch, tas, synth)
 
-    traffic = committed_traffic("decode_split_kernel_traffic.txt",
+    traffic = committed_traffic("decode_ragged_b64_traffic.txt",
                                 "decode.hip")
     roofline = {
-        "kernel": "decode_split_kernel+decode_combine_kernel (one attn_decode call)",
+        "kernel": "decode_bf16_kernel<128,4> + decode_combine_kernel (one attn_decode call)",
         "bound": "hbm", "achieved": round(dec_gbps, 1),
         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
