@@ -161,9 +161,41 @@ def bench_single_position(torch, tas, synth, copies=32, reps=20):
     ref = out.float().cpu().numpy()
     assert np.all(np.isfinite(ref))
     del ks, vs
+    # Time against position (warm, one cache): the work of a call is
+    # proportional to the valid rows, so the time should be affine in p+1.
+    sweep = []
+    for pp in (0, 100, 1000, 4000, 8000):
+        with torch.cuda.stream(s):
+            for _ in range(4):
+                tas.attn_decode(q, k0, v0, position_id=pp, scale=p["scale"],
+                                out=out, workspace=ws)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(copies):
+                tas.attn_decode(q, k0, v0, position_id=pp, scale=p["scale"],
+                                out=out, workspace=ws)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        sweep.append((pp, e0.elapsed_time(e1) * 1e3 / (reps * copies)))
+        del g
+    xs = np.array([pp + 1 for pp, _ in sweep], dtype=np.float64)
+    ys = np.array([us for _, us in sweep])
+    slope, icpt = np.polyfit(xs[1:], ys[1:], 1)  # p >= 100
     torch.cuda.empty_cache()
     return dict(workload="decode_gqa_static_pos8000", bytes=nbytes,
-                calls_per_graph=copies, **res)
+                calls_per_graph=copies, **res,
+                warm_us_by_position={str(pp): round(us, 3) for pp, us in sweep},
+                warm_fit_us=dict(per_1000_rows=round(slope * 1000, 4),
+                                 intercept=round(icpt, 3)))
 
 
 # ----------------------------------------------------------------------------

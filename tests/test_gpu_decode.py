@@ -150,6 +150,26 @@ def test_decode_edge_lengths_clamped():
     assert err <= tol("f32"), err
 
 
+@pytest.mark.parametrize("B", [63, 65, 256, 300])
+def test_decode_many_sequences_with_zero_lengths(B):
+    # Batches around the sizes where the ragged work order changes (one or
+    # more 64-sequence chunks of the on-device scan; above 256 sequences the
+    # plain grid order is used), with every length category present: zero,
+    # shorter than one split, whole splits, and whole splits plus a tail.
+    rng = np.random.default_rng(B)
+    lens = rng.integers(0, 200, B).astype(np.int32)
+    lens[::7] = 0
+    lens[1::11] = 64
+    lens[2::13] = 128
+    inp = synth.decode_ragged(30 + B, B=B, Hq=4, Hkv=2, D=64, max_length=200,
+                              dtype="bf16", lengths=lens)
+    say(f"decode bf16 ragged B={B} with zero lengths, split_rows=64")
+    out = to_host64(run_decode(inp, split_rows=64))
+    assert np.all(out[lens == 0] == 0)
+    err = max_abs_err(out, oracle_of(inp))
+    assert err <= tol("bf16"), err
+
+
 def test_decode_position_is_last_row():
     inp = synth.decode_uniform(23, B=2, Hq=16, Hkv=4, D=128, max_length=777,
                                position_id=776, dtype="bf16")
