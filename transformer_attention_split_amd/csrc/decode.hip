@@ -266,28 +266,30 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   float m = kNegInf;
   float lsum = 0.f;
 
-  for (int t0 = it.row0 + w * BN; t0 < it.row1; t0 += 4 * BN) {
-    const bool full = t0 + BN <= it.row1;
-    // ---- loads: K in the A-operand layout, V as 8-row groups ----------------
-    u32x4_t kf[NKB][KS];
+  // Tiles of this wave: t0 = row0 + w*BN + 4*BN*i. The next tile's K is
+  // loaded as soon as the score products have read the current K registers,
+  // and its V as soon as the current V rows are in LDS, so both loads run
+  // during the softmax and P·V of this tile. Rows are clamped to the split
+  // (a partial last tile reads valid rows; they are masked).
+  const int last_row = it.row1 - 1;
+  u32x4_t kf[NKB][KS], vr[8];
+  auto load_k = [&](int t0) {
 #pragma unroll
     for (int kb16 = 0; kb16 < NKB; ++kb16) {
-      const int row = t0 + kb16 * 16 + li;
+      const int row = min(t0 + kb16 * 16 + li, last_row);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (full || row < it.row1) v = ldnt(kb + (size_t)row * D + ks * 32 + 8 * lg);
-        kf[kb16][ks] = v;
-      }
+      for (int ks = 0; ks < KS; ++ks) kf[kb16][ks] = ldnt(kb + (size_t)row * D + ks * 32 + 8 * lg);
     }
-    u32x4_t vr[8];
+  };
+  auto load_v = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = t0 + 8 * oct + i;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (full || row < it.row1) v = ldnt(vb + (size_t)row * D + 8 * ch);
-      vr[i] = v;
+      const int row = min(t0 + 8 * oct + i, last_row);
+      vr[i] = ldnt(vb + (size_t)row * D + 8 * ch);
     }
+  };
+  auto compute_tile = [&](int t0, int tnext) {
+    const bool full = t0 + BN <= it.row1;
     // ---- Sᵀ = K·Qᵀ --------------------------------------------------------------
     f32x4_t sc[NKB];
 #pragma unroll
@@ -298,6 +300,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
         sc[kb16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(kf[kb16][ks]), qf[ks], sc[kb16], 0, 0, 0);
     }
+    if (tnext >= 0) load_k(tnext);
     // ---- V rows -> Vᵀ in LDS (keys 8*oct..8*oct+7 of dims 8*ch..8*ch+7) ----
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -314,6 +317,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
       dst[0] = u32x2_t{pk[0], pk[1]};
       dst[1] = u32x2_t{pk[2], pk[3]};
     }
+    if (tnext >= 0) load_v(tnext);
     // ---- online softmax -----------------------------------------------------------
     float mx = kNegInf;
 #pragma unroll
@@ -366,6 +370,14 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  for (int t0 = it.row0 + w * BN, first = 1; t0 < it.row1; t0 += 4 * BN, first = 0) {
+    if (first) {
+      load_k(t0);
+      load_v(t0);
+    }
+    const int t1 = t0 + 4 * BN;
+    compute_tile(t0, t1 < it.row1 ? t1 : -1);
   }
 
   // ---- merge the 4 waves -----------------------------------------------------------
