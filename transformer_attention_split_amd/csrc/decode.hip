@@ -41,8 +41,9 @@
 // either writes the output directly (the sequence has a single split) or
 // writes one partial (running max, running sum, unnormalised output) per
 // query head to the workspace. decode_combine_kernel then merges the
-// partials of every multi-split sequence in split order (log-sum-exp),
-// divides by the total sum and casts to the output type. (Merging inside the
+// partials of every multi-split sequence (log-sum-exp: each partial weighted
+// by exp of its running max less the largest), divides by the total sum and
+// casts to the output type. (Merging inside the
 // split kernel, in the last workgroup to finish, needs device-scope fences
 // per workgroup and a serial merge; both measured far slower than the
 // second launch.)
@@ -581,60 +582,98 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(
 // in split order with independent (unrolled) loads.
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int D, int G>
-__global__ __launch_bounds__(64 * G) void decode_combine_kernel(
+// One wave per (query head, sequence). The loads of the first 64 partial
+// outputs are issued before the running maxima and sums are read, so a
+// sequence with up to 64 splits is merged after a single memory round trip;
+// further chunks of 64 follow one round trip each. Lane l holds output
+// dimensions [l*D/64, (l+1)*D/64); the weight of split t sits in lane t % 64
+// of its chunk and is broadcast with a lane read.
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void decode_combine_kernel(
     const float *__restrict__ ws_ml, const float *__restrict__ ws_o,
     const int32_t *__restrict__ seq_lens, int position_id,
     void *__restrict__ outp, int Hq, int max_length, int split_rows,
     int splits) {
   constexpr int PER = D / 64;  // output dimensions per lane
-  __shared__ float wsh[G][kDecodeMaxSplits];
-  const int g = blockIdx.x;
+  static_assert(PER == 1 || PER == 2, "D is 64 or 128");
+  const int hq = blockIdx.x;
   const int b = blockIdx.y;
   const Item it = make_item(seq_lens, b, position_id, max_length, split_rows, 0);
   const int n = it.n_split;
   if (n <= 1) return;  // finished by the split kernel (or zero rows)
-  const int h = threadIdx.x / 64;
-  const int lane = threadIdx.x % 64;
-  const size_t head = (size_t)b * Hq + (size_t)g * G + h;
-  const float *ml = ws_ml + head * splits * 2;
-  float mx = kNegInf;
-  for (int t = lane; t < n; t += 64) mx = fmaxf(mx, ml[2 * t]);
+  const int lane = threadIdx.x;
+  const size_t head = (size_t)b * Hq + hq;
+  const float2 *ml = reinterpret_cast<const float2 *>(ws_ml + head * splits * 2);
+  const float *o = ws_o + head * splits * D + lane * PER;
+  const int last = n - 1;
+  // Partials t >= n are never written: their loads are clamped to split n-1
+  // (finite) and their weight is 0.
+  float v[64][PER];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (c0 + 16 * q < n) {
+#pragma unroll
+        for (int u = 16 * q; u < 16 * q + 16; ++u) {
+          const float *src = o + (size_t)min(c0 + u, last) * D;
+          if constexpr (PER == 2) {
+            const float2 x = *reinterpret_cast<const float2 *>(src);
+            v[u][0] = x.x;
+            v[u][1] = x.y;
+          } else {
+            v[u][0] = src[0];
+          }
+        }
+      }
+    }
+  };
+  load_chunk(0);
+  const float2 ml0 = ml[min(lane, last)];
+  float mx = ml0.x;
+  for (int t = lane + 64; t < n; t += 64) mx = fmaxf(mx, ml[t].x);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  float lt = 0.f;
-  for (int t = lane; t < n; t += 64) {
-    const float w = fast_exp2(ml[2 * t] - mx);
-    wsh[h][t] = w;
-    lt = fmaf(w, ml[2 * t + 1], lt);
+  float wl = lane < n ? fast_exp2(ml0.x - mx) : 0.f;
+  float lt = wl * ml0.y;
+  for (int t = lane + 64; t < n; t += 64) {
+    const float2 x = ml[t];
+    lt = fmaf(fast_exp2(x.x - mx), x.y, lt);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lt += __shfl_xor(lt, off);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const float *o = ws_o + head * splits * D + lane * PER;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  int t = 0;
-  for (; t + 8 <= n; t += 8) {
-    float v[8][PER];
+  for (int c0 = 0;;) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int q = 0; q < 4; ++q) {
+      if (c0 + 16 * q < n) {
 #pragma unroll
-      for (int e = 0; e < PER; ++e) v[u][e] = o[(size_t)(t + u) * D + e];
+        for (int u = 16 * q; u < 16 * q + 16; ++u) {
+          const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wsh[h][t + u], v[u][e], acc[e]);
+          for (int e = 0; e < PER; ++e) acc[e] = fmaf(wt, v[u][e], acc[e]);
+        }
+      }
+    }
+    c0 += 64;
+    if (c0 >= n) break;
+    load_chunk(c0);
+    const int t = c0 + lane;
+    wl = t < n ? fast_exp2(ml[min(t, last)].x - mx) : 0.f;
   }
-  for (; t < n; ++t)
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wsh[h][t], o[(size_t)t * D + e], acc[e]);
   const float inv = 1.f / lt;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) store_out<BF16>(outp, head * D + lane * PER + e, acc[e] * inv);
+  const size_t oi = head * D + lane * PER;
+  if constexpr (PER == 2) {
+    if constexpr (BF16) {
+      static_cast<uint32_t *>(outp)[oi / 2] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+      *reinterpret_cast<float2 *>(static_cast<float *>(outp) + oi) =
+          make_float2(acc[0] * inv, acc[1] * inv);
+    }
+  } else {
+    store_out<BF16>(outp, oi, acc[0] * inv);
+  }
 }
 
 template <bool BF16, int D, int G>
@@ -655,7 +694,7 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.splits <= 1) return e;
-  decode_combine_kernel<BF16, D, G><<<dim3(a.Hkv, a.B), 64 * G, 0, stream>>>(
+  decode_combine_kernel<BF16, D><<<dim3(a.Hq, a.B), 64, 0, stream>>>(
       a.ws_ml, a.ws_o, a.seq_lens, a.position_id, a.out, a.Hq, a.max_length,
       a.plan.split_rows, a.plan.splits);
   return hipGetLastError();
