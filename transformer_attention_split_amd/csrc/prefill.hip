@@ -644,51 +644,58 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
   }
 
   // ---- merge the key quarters of each query group (log-sum-exp), store -----------
-  // outputs [NQG][NKQ][NQW][D] in kb0 (group 0) and kb1 (group 1); running
-  // max and sum [NQG][NKQ][NQW] in vb0
-  auto mo_of = [&](int grp, int kk) {
-    return reinterpret_cast<float *>((grp == 0 ? kb0 : kb1) + kk * NQW * D * 4);
-  };
-  float *mm = reinterpret_cast<float *>(vb0);  // [NQG][NKQ][NQW]
-  float *ml = mm + NQG * NKQ * NQW;            // [NQG][NKQ][NQW]
-  {
-    float *mo = mo_of(qgi, kq);
+  // 1. running max and sum of every (group, query, quarter) -> mm, ml
+  //    [NQG][NQW][NKQ] in vb0;
+  // 2. each wave weights its own output by exp2(m - M) / L (M, L over the
+  //    four quarters of the query) and writes it as fp32 [NKQ][NQW][D] into
+  //    kb0 (group 0) / kb1 (group 1), 16-byte chunk c of row qi at position
+  //    c ^ (qi % 16), so the 16 rows of one write fall on distinct banks;
+  // 3. every thread adds the four quarters of 4 consecutive outputs and stores
+  //    them as bf16.
+  float *mm = reinterpret_cast<float *>(vb0);  // [NQG][NQW][NKQ]
+  float *ml = mm + NQG * NQW * NKQ;            // [NQG][NQW][NKQ]
+  if (lg == 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int qi = nb * 16 + li;  // query inside the group
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        *reinterpret_cast<f32x4_t *>(mo + qi * D + db * 16 + 4 * lg) = o[nb][db];
-      if (lg == 0) {
-        mm[(qgi * NKQ + kq) * NQW + qi] = mc[nb];
-        ml[(qgi * NKQ + kq) * NQW + qi] = lacc[nb][0];
-      }
+      const int qi = nb * 16 + li;
+      mm[(qgi * NQW + qi) * NKQ + kq] = mc[nb];
+      ml[(qgi * NQW + qi) * NKQ + kq] = lacc[nb][0];
     }
   }
   __syncthreads();
-  for (int i = tid; i < BM * D / 2; i += T::THREADS) {
-    const int q = (2 * i) / D;       // query inside the workgroup
-    const int d = (2 * i) % D;       // even dimension; this thread does d, d+1
+  {
+    float *mo = reinterpret_cast<float *>(qgi == 0 ? kb0 : kb1) + kq * NQW * D;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int qi = nb * 16 + li;
+      const f32x4_t m4 = *reinterpret_cast<const f32x4_t *>(&mm[(qgi * NQW + qi) * NKQ]);
+      const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(&ml[(qgi * NQW + qi) * NKQ]);
+      const float M = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      float L = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKQ; ++kk)
+        // a key quarter that saw no key of this query contributes nothing
+        L = fmaf(m4[kk] == kNegInf ? 0.f : fast_exp2(m4[kk] - M), l4[kk], L);
+      // (a query past the end of the sequence has L = 0; it is not stored)
+      const float wgt = mc[nb] == kNegInf ? 0.f : fast_exp2(mc[nb] - M) / L;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *reinterpret_cast<f32x4_t *>(mo + qi * D + (((db * 4 + lg) ^ li) * 4)) = o[nb][db] * wgt;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < BM * D / 4; i += T::THREADS) {
+    const int q = i / (D / 4);   // query inside the workgroup
+    const int c = i % (D / 4);   // 16-byte chunk: outputs 4c .. 4c+3
     const int grp = q / NQW, qi = q % NQW;
     const int qglob = qt * BM + q;
     if (qglob >= Lq) continue;
-    float M = kNegInf;
+    const float *mo = reinterpret_cast<const float *>(grp == 0 ? kb0 : kb1) + qi * D + ((c ^ (qi % 16)) * 4);
+    f32x4_t acc = *reinterpret_cast<const f32x4_t *>(mo);
 #pragma unroll
-    for (int kk = 0; kk < NKQ; ++kk) M = fmaxf(M, mm[(grp * NKQ + kk) * NQW + qi]);
-    float a0 = 0.f, a1 = 0.f, lt = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < NKQ; ++kk) {
-      const float mk = mm[(grp * NKQ + kk) * NQW + qi];
-      // a key quarter that saw no key of this query contributes nothing
-      const float wgt = mk == kNegInf ? 0.f : fast_exp2(mk - M);
-      const float *src = mo_of(grp, kk) + qi * D + d;
-      a0 = fmaf(wgt, src[0], a0);
-      a1 = fmaf(wgt, src[1], a1);
-      lt = fmaf(wgt, ml[(grp * NKQ + kk) * NQW + qi], lt);
-    }
-    const float inv = 1.f / lt;
-    *reinterpret_cast<uint32_t *>(outg + ((size_t)j * Lq + qglob) * D + d) =
-        pack_bf16x2(a0 * inv, a1 * inv);
+    for (int kk = 1; kk < NKQ; ++kk) acc += *reinterpret_cast<const f32x4_t *>(mo + kk * NQW * D);
+    *reinterpret_cast<u32x2_t *>(outg + ((size_t)j * Lq + qglob) * D + 4 * c) =
+        u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
   }
 }
 
