@@ -7,6 +7,7 @@ never import it, and it imports nothing from them.
 from .attention import (  # noqa: F401
     default_scale,
     decode,
+    decode_append,
     decode_sequence,
     prefill,
     topk_sparse,

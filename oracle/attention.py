@@ -106,6 +106,37 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     return out
 
 
+def decode_append(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+                  k_cache: np.ndarray, v_cache: np.ndarray,
+                  position_id: Optional[int] = None,
+                  seq_lens: Optional[np.ndarray] = None,
+                  scale: Optional[float] = None):
+    """The patched ``forward_step`` order [P1 §4.1]: first store the current
+    token's key and value at its cache row, then attend over the valid rows.
+
+    k_new, v_new: [B, Hkv, D]. The row of sequence b is ``position_id``, or
+    ``seq_lens[b] - 1`` for a ragged batch (lengths clamped to
+    [0, max_length]; a length-0 sequence has no current token, so nothing is
+    stored — reading). Returns (out, k_cache', v_cache') with the caches
+    copied, not modified in place.
+    """
+    B = q.shape[0]
+    max_length = k_cache.shape[2]
+    k2 = np.array(k_cache, copy=True)
+    v2 = np.array(v_cache, copy=True)
+    for b in range(B):
+        if seq_lens is None:
+            r = position_id
+        else:
+            r = int(min(max(int(seq_lens[b]), 0), max_length)) - 1
+        if r >= 0:
+            k2[b, :, r, :] = k_new[b]
+            v2[b, :, r, :] = v_new[b]
+    out = decode(q, k2, v2, position_id=position_id, seq_lens=seq_lens,
+                 scale=scale)
+    return out, k2, v2
+
+
 # ----------------------------------------------------------------------------
 # Causal prefill against a cached prefix  [P2 solution section]
 # ----------------------------------------------------------------------------

@@ -154,6 +154,13 @@ def iter_ragged(seed: int, B: int, Hq: int, Hkv: int, D: int,
         yield (b, L) + ragged_sequence(seed, b, Hq, Hkv, D, L, dtype)
 
 
+def new_token_kv(seed: int, B: int, Hkv: int, D: int, dtype: str):
+    """(k_new, v_new), each [B, Hkv, D]: the current token's key and value for
+    a fused append."""
+    rng = np.random.default_rng([seed, 10**6])
+    return _draw(rng, (B, Hkv, D), dtype), _draw(rng, (B, Hkv, D), dtype)
+
+
 # ----------------------------------------------------------------------------
 # Prefill inputs
 # ----------------------------------------------------------------------------

@@ -146,6 +146,57 @@ def test_decode_matches_torch_sdpa_on_sliced_cache(B, Hq, Hkv, D, M, p):
     np.testing.assert_allclose(out2, ref2, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("p", [0, 5, 11])
+def test_decode_append_follows_the_page_forward_step(p):
+    # [P1 §4.1]: key_cache[:, :, position_id, :] = key_states (same for V),
+    # then SDPA over the slice [0, position_id] with enable_gqa. Row p of the
+    # incoming caches holds NaN: only the stored values may reach the output.
+    rng = np.random.default_rng(500 + p)
+    B, Hq, Hkv, D, M = 2, 4, 2, 8, 12
+    q = rng.standard_normal((B, Hq, D))
+    kn = rng.standard_normal((B, Hkv, D))
+    vn = rng.standard_normal((B, Hkv, D))
+    k = rng.standard_normal((B, Hkv, M, D))
+    v = rng.standard_normal((B, Hkv, M, D))
+    k[:, :, p] = np.nan
+    v[:, :, p] = np.nan
+    out, k2, v2 = oracle.decode_append(q, kn, vn, k, v, position_id=p)
+    kt, vt = _t(k).clone(), _t(v).clone()
+    kt[:, :, p, :] = _t(kn)
+    vt[:, :, p, :] = _t(vn)
+    ref = _sdpa_sliced(q, kt.numpy(), vt.numpy(), p + 1)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(k2, kt.numpy())
+    np.testing.assert_array_equal(v2, vt.numpy())
+    assert np.isnan(k[:, :, p]).all()  # the inputs are not modified
+
+
+def test_decode_append_ragged_rows_and_empty_sequence():
+    rng = np.random.default_rng(77)
+    B, Hq, Hkv, D, M = 3, 2, 1, 4, 6
+    q = rng.standard_normal((B, Hq, D))
+    kn = rng.standard_normal((B, Hkv, D))
+    vn = rng.standard_normal((B, Hkv, D))
+    k = rng.standard_normal((B, Hkv, M, D))
+    v = rng.standard_normal((B, Hkv, M, D))
+    lens = np.array([0, 1, 6])
+    out, k2, v2 = oracle.decode_append(q, kn, vn, k, v, seq_lens=lens)
+    # length 0: nothing stored, zero output
+    np.testing.assert_array_equal(k2[0], k[0])
+    assert np.all(out[0] == 0)
+    # otherwise the new token is the last valid row, the rest is untouched
+    for b, r in ((1, 0), (2, 5)):
+        np.testing.assert_array_equal(k2[b, :, r], kn[b])
+        np.testing.assert_array_equal(v2[b, :, r], vn[b])
+        keep = [i for i in range(M) if i != r]
+        np.testing.assert_array_equal(k2[b][:, keep], k[b][:, keep])
+        ref = _sdpa_sliced(q[b:b + 1], k2[b:b + 1], v2[b:b + 1], int(lens[b]))
+        np.testing.assert_allclose(out[b:b + 1], ref, rtol=0, atol=1e-12)
+    # length 1 attends to the new row alone: output = v_new
+    np.testing.assert_allclose(out[1], np.repeat(vn[1], Hq, axis=0),
+                               rtol=0, atol=1e-15)
+
+
 def test_decode_sliced_equals_masked_full_cache():
     # The page's original form: full cache, bool mask arange(max) <= pos.
     rng = np.random.default_rng(2)
