@@ -199,6 +199,44 @@ def bench_single_position(torch, tas, synth, copies=32, reps=20):
 
 
 # ----------------------------------------------------------------------------
+# Secondary: the cache append fused into the decode call
+# ----------------------------------------------------------------------------
+def bench_append(torch, tas, dec, steps):
+    """attn_decode_append on the ragged batch (each call stores one new K/V
+    row per (sequence, kv head) and attends to it) against attn_decode on the
+    same inputs, alternating calls, HIP events around each. The caches keep
+    the appended rows afterwards; the decode output buffer is not touched."""
+    import numpy as np
+    p = dec["p"]
+    B, Hkv, D = p["B"], p["Hkv"], p["D"]
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    k_new = torch.randn(B, Hkv, D, device="cuda", generator=g).bfloat16()
+    v_new = torch.randn(B, Hkv, D, device="cuda", generator=g).bfloat16()
+    out = torch.empty_like(dec["out"])
+    kw = dict(seq_lens=dec["seq_lens"], scale=p["scale"], out=out,
+              workspace=dec["ws"])
+    for _ in range(5):
+        tas.attn_decode_append(dec["q"], k_new, v_new, dec["k"], dec["v"], **kw)
+        tas.attn_decode(dec["q"], dec["k"], dec["v"], **kw)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+          for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        tas.attn_decode_append(dec["q"], k_new, v_new, dec["k"], dec["v"], **kw)
+        e[1].record()
+        tas.attn_decode(dec["q"], dec["k"], dec["v"], **kw)
+        e[2].record()
+    torch.cuda.synchronize()
+    ta = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in ev]))
+    td = float(np.median([e[1].elapsed_time(e[2]) * 1e3 for e in ev]))
+    return dict(workload="decode_ragged_b64 + append of one row per "
+                         "(sequence, kv head)",
+                us_p50_append_decode=round(ta, 2), us_p50_decode=round(td, 2),
+                GBps_append_decode=round(dec["bytes"] / (ta * 1e-6) / 1e9, 1))
+
+
+# ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the decode workload
 # ----------------------------------------------------------------------------
 def cpu_baseline(dec, synth, budget_s):
@@ -228,8 +266,25 @@ def cpu_baseline(dec, synth, budget_s):
         done += 1
         if t_total >= budget_s:
             break
+    # the same oracle on one BLAS thread, over the first sequence
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        L = int(lens[0])
+        qb, kb, vb = synth.ragged_sequence(p["seed"], 0, p["Hq"], p["Hkv"],
+                                           p["D"], L, "bf16")
+        qf, kf, vf = (synth.bf16_to_f32(x) for x in (qb, kb, vb))
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.decode_sequence(qf, kf, vf, L, p["scale"])
+            t1 = time.perf_counter() - t0
+        nb1 = 2 * p["Hkv"] * p["D"] * 2 * L + 2 * p["Hq"] * p["D"] * 2
+        single = dict(value=round(nb1 / t1 / 1e9, 4), unit="GB/s", cores=1,
+                      sample=f"sequence 0 ({L} rows, {nb1} bytes) in {t1:.2f} s")
+    except Exception as exc:  # pragma: no cover
+        single = dict(error=str(exc))
     return dict(value=round(nbytes / t_total / 1e9, 4), unit="GB/s",
-                cores=int(threads), kind="oracle",
+                cores=int(threads), kind="oracle", single_thread=single,
                 sample=(f"fp64 NumPy oracle over the first {done} of 64 "
                         f"sequences of the ragged decode batch "
                         f"({nbytes} algorithmic bytes in {t_total:.2f} s)"),
@@ -325,6 +380,11 @@ def main():
     t_dec = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3
     t_pre = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
     t_tk = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps * 1e-3
+    def pct(i):
+        xs = np.array([e[i].elapsed_time(e[i + 1]) * 1e3 for e in evs])
+        return {k: round(float(np.percentile(xs, q)), 2)
+                for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
+    dec_pct, pre_pct, tk_pct = pct(0), pct(1), pct(2)
     dec_gbps = dec["bytes"] / t_dec / 1e9
     pre_tflops = pre["flops"] / t_pre / 1e12
     tk_tflops = tk["flops"] / t_tk / 1e12
@@ -337,12 +397,16 @@ def main():
                         TFLOPs=round(pre_tflops, 2),
                         frac_of_bf16_mfma_peak=round(
                             pre_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                        flops=pre["flops"]),
+                        flops=pre["flops"], us_percentiles=pre_pct),
         "topk": dict(workload="topk_c2psa", us=round(t_tk * 1e6, 2),
                      TFLOPs=round(tk_tflops, 3),
                      frac_of_fp64_peak=round(tk_tflops / FP64_PEAK_TFLOPS, 4),
-                     flops=tk["flops"]),
+                     flops=tk["flops"], us_percentiles=tk_pct),
     }
+    if not args.no_secondary:
+        log("fused append + decode on the ragged batch ...")
+        secondary["decode_append_ragged_b64"] = bench_append(torch, tas, dec,
+                                                             args.steps)
     if not args.no_secondary:
         log("single-sequence position-8000 decode (graph replay) ...")
         secondary["decode_single_pos8000"] = bench_single_position(
@@ -351,13 +415,14 @@ def main():
     traffic = committed_traffic("decode_ragged_b64_traffic.txt",
                                 "decode.hip")
     roofline = {
-        "kernel": "decode_bf16_kernel<128,4> + decode_combine_kernel (one attn_decode call)",
+        "kernel": "decode_bf16_kernel<128,4,false> + decode_combine_kernel<true,128> (one attn_decode call)",
         "bound": "hbm", "achieved": round(dec_gbps, 1),
         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
         "traffic": traffic,
         "algorithmic_bytes_per_launch": dec["bytes"],
         "avg_launch_us": round(t_dec * 1e6, 2),
+        "launch_us_percentiles": dec_pct,
     }
     cpu = None
     if not args.no_cpu_baseline:

@@ -1,8 +1,8 @@
 /*
  * attn.h — C ABI of the MI355X (gfx950) KV-cache attention library.
  *
- * Three operations, each one asynchronous launch sequence on the caller's
- * HIP stream:
+ * Three operations (plus decode with a fused cache append), each one
+ * asynchronous launch sequence on the caller's HIP stream:
  *
  *   attn_decode   single-token decode over a statically preallocated cache,
  *                 attending to rows [0, position_id] (or [0, seq_lens[b]) for
@@ -121,6 +121,35 @@ int attn_decode(int dtype, const void *q, const void *k_cache,
                 int max_length, int position_id, const int32_t *seq_lens,
                 float scale, int split_rows, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/* Fused append + decode: stores the current token's K/V into the caches and
+ * attends to it in the same launch sequence (one split launch, plus the
+ * combine launch when a sequence has several splits). The pages write k_new
+ * and v_new into the static cache at position_id and then run the attention
+ * over rows [0, position_id] ("MiniCPM4 forward_step Attention Performance
+ * Fix", §4.1, the patched forward_step: cache update, then SDPA over the
+ * slice); this call does both.
+ *
+ *   k_new,
+ *   v_new      [B][Hkv][D], same dtype as q; not modified.
+ *   k_cache,
+ *   v_cache    as for attn_decode, but written: row r_b of sequence b, with
+ *              r_b = position_id (seq_lens == NULL) or seq_lens[b] - 1 (after
+ *              the clamp to [0, max_length]; a sequence of length 0 gets no
+ *              append), receives k_new[b] / v_new[b] for every kv head.
+ *              Other rows are not written.
+ * Every other argument, the result and the supported set are those of
+ * attn_decode: the output equals attn_decode on the caches after the append
+ * (the appended row's values are read from k_new / v_new, so the cache write
+ * and the reads of that row do not race). k_new / v_new must not alias the
+ * caches or out. ATTN_E_ARG if B > 0 and k_new or v_new is NULL or not
+ * 16-byte aligned. */
+int attn_decode_append(int dtype, const void *q, const void *k_new,
+                       const void *v_new, void *k_cache, void *v_cache,
+                       void *out, int B, int Hq, int Hkv, int D, int max_length,
+                       int position_id, const int32_t *seq_lens, float scale,
+                       int split_rows, void *workspace, size_t workspace_bytes,
+                       void *stream);
 
 /* --------------------------------------------------------------------------
  * Prefill

@@ -107,6 +107,38 @@ def test_decode_batch_zero_is_a_noop():
     assert decode(B=0, ws=None, ws_bytes=0) == OK
 
 
+def decode_append(**kw):
+    a = dict(dtype=BF16, q=P, kn=P, vn=P, k=P, v=P, out=P, B=1, Hq=32, Hkv=8,
+             D=128, max_length=8192, position_id=100, seq_lens=None,
+             scale=0.088, split_rows=0, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_decode_append(a["dtype"], a["q"], a["kn"], a["vn"], a["k"],
+                                  a["v"], a["out"], a["B"], a["Hq"], a["Hkv"],
+                                  a["D"], a["max_length"], a["position_id"],
+                                  a["seq_lens"], a["scale"], a["split_rows"],
+                                  a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), E_ARG),
+    (dict(vn=None), E_ARG),
+    (dict(kn=P + 8), E_ARG),
+    (dict(vn=P + 2), E_ARG),
+    # the checks shared with attn_decode apply too
+    (dict(D=96), E_UNSUP),
+    (dict(position_id=8192), E_ARG),
+    (dict(k=None), E_ARG),
+    (dict(ws=None), E_WS),
+])
+def test_decode_append_rejects(kw, status):
+    assert decode_append(**kw) == status
+    assert lib.attn_last_error().decode().startswith("attn_decode_append")
+
+
+def test_decode_append_batch_zero_is_a_noop():
+    assert decode_append(B=0, kn=None, vn=None, ws=None, ws_bytes=0) == OK
+
+
 def test_decode_workspace_bound():
     ws = lib.attn_decode_workspace_bytes
     assert ws(0, 32, 8, 128, 8192, 0) == 0

@@ -15,11 +15,12 @@ from ._binding import (  # noqa: F401
     AttnArgError,
     AttnError,
     attn_decode,
+    attn_decode_append,
     attn_decode_workspace_bytes,
     attn_prefill,
     attn_topk,
     lib,
 )
 
-__all__ = ["attn_decode", "attn_prefill", "attn_topk",
+__all__ = ["attn_decode", "attn_decode_append", "attn_prefill", "attn_topk",
            "attn_decode_workspace_bytes", "AttnError", "AttnArgError"]

@@ -44,6 +44,9 @@ lib.attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
 lib.attn_decode.restype = _i
 lib.attn_decode.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p,
                             _f, _i, _p, _sz, _p]
+lib.attn_decode_append.restype = _i
+lib.attn_decode_append.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i,
+                                   _i, _i, _p, _f, _i, _p, _sz, _p]
 lib.attn_prefill.restype = _i
 lib.attn_prefill.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
                              _f, _p]
@@ -51,8 +54,8 @@ lib.attn_topk.restype = _i
 lib.attn_topk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 
 EXPORTED = ("attn_status_str", "attn_last_error", "attn_abi_version",
-            "attn_decode_workspace_bytes", "attn_decode", "attn_prefill",
-            "attn_topk")
+            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_append",
+            "attn_prefill", "attn_topk")
 
 
 class AttnError(RuntimeError):
@@ -112,16 +115,10 @@ def attn_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int,
                                                split_rows))
 
 
-def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                *, position_id: Optional[int] = None,
-                seq_lens: Optional[torch.Tensor] = None,
-                scale: Optional[float] = None, split_rows: int = 0,
-                out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None,
-                stream=None) -> torch.Tensor:
-    """Single-token decode. q [B,Hq,D]; caches [B,Hkv,max_length,D];
-    exactly one of ``position_id`` (rows [0, position_id]) or ``seq_lens``
-    (int32 [B] on the GPU, rows [0, seq_lens[b])). Returns out [B,Hq,D]."""
+def _decode_args(q, k_cache, v_cache, position_id, seq_lens, scale,
+                 split_rows, out, workspace):
+    """Shared checks of attn_decode / attn_decode_append; returns the
+    marshalled sizes, scale, out and workspace."""
     _need_dense("q", q, 3)
     _need_dense("k_cache", k_cache, 4)
     _need_dense("v_cache", v_cache, 4)
@@ -152,13 +149,58 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8,
                                 device=q.device)
+    return B, Hq, Hkv, D, max_length, float(scale), out, workspace
+
+
+def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                *, position_id: Optional[int] = None,
+                seq_lens: Optional[torch.Tensor] = None,
+                scale: Optional[float] = None, split_rows: int = 0,
+                out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """Single-token decode. q [B,Hq,D]; caches [B,Hkv,max_length,D];
+    exactly one of ``position_id`` (rows [0, position_id]) or ``seq_lens``
+    (int32 [B] on the GPU, rows [0, seq_lens[b])). Returns out [B,Hq,D]."""
+    B, Hq, Hkv, D, max_length, scale, out, workspace = _decode_args(
+        q, k_cache, v_cache, position_id, seq_lens, scale, split_rows, out,
+        workspace)
     st = lib.attn_decode(_dtype_code(q), _ptr(q), _ptr(k_cache),
                          _ptr(v_cache), _ptr(out), B, Hq, Hkv, D, max_length,
                          -1 if position_id is None else int(position_id),
-                         _ptr(seq_lens), float(scale), int(split_rows),
+                         _ptr(seq_lens), scale, int(split_rows),
                          _ptr(workspace), workspace.numel(),
                          _stream_handle(stream))
     _check(st, "attn_decode")
+    return out
+
+
+def attn_decode_append(q: torch.Tensor, k_new: torch.Tensor,
+                       v_new: torch.Tensor, k_cache: torch.Tensor,
+                       v_cache: torch.Tensor, *,
+                       position_id: Optional[int] = None,
+                       seq_lens: Optional[torch.Tensor] = None,
+                       scale: Optional[float] = None, split_rows: int = 0,
+                       out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Fused append + decode: k_new / v_new [B,Hkv,D] are stored at row
+    position_id (or seq_lens[b]-1) of the caches, which are updated in place,
+    and the result equals attn_decode on the updated caches."""
+    B, Hq, Hkv, D, max_length, scale, out, workspace = _decode_args(
+        q, k_cache, v_cache, position_id, seq_lens, scale, split_rows, out,
+        workspace)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need_dense(name, t, 3)
+        if tuple(t.shape) != (B, Hkv, D) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [{B},{Hkv},{D}] {q.dtype}")
+    st = lib.attn_decode_append(
+        _dtype_code(q), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+        _ptr(v_cache), _ptr(out), B, Hq, Hkv, D, max_length,
+        -1 if position_id is None else int(position_id), _ptr(seq_lens),
+        scale, int(split_rows), _ptr(workspace), workspace.numel(),
+        _stream_handle(stream))
+    _check(st, "attn_decode_append")
     return out
 
 

@@ -142,52 +142,61 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D,
   return ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S, D);
 }
 
-int attn_decode(int dtype, const void *q, const void *k_cache,
-                const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
-                int max_length, int position_id, const int32_t *seq_lens,
-                float scale, int split_rows, void *workspace,
-                size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launch shared by attn_decode and attn_decode_append (fn names
+// the entry point in error messages; k_new == nullptr: plain decode).
+int decode_impl(const char *fn, int dtype, const void *q, const void *k_new,
+                const void *v_new, const void *k_cache, const void *v_cache,
+                void *out, int B, int Hq, int Hkv, int D, int max_length,
+                int position_id, const int32_t *seq_lens, float scale,
+                int split_rows, void *workspace, size_t workspace_bytes,
+                void *stream) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16)
-    return fail(ATTN_E_ARG, "attn_decode: unknown dtype %d", dtype);
+    return fail(ATTN_E_ARG, "%s: unknown dtype %d", fn, dtype);
   if (B < 0 || B > 65535)
-    return fail(ATTN_E_ARG, "attn_decode: B=%d outside [0, 65535]", B);
+    return fail(ATTN_E_ARG, "%s: B=%d outside [0, 65535]", fn, B);
   if (Hq < 1 || Hkv < 1 || Hkv > 65535)
-    return fail(ATTN_E_ARG, "attn_decode: Hq=%d Hkv=%d must be >= 1 (Hkv <= 65535)", Hq, Hkv);
+    return fail(ATTN_E_ARG, "%s: Hq=%d Hkv=%d must be >= 1 (Hkv <= 65535)", fn, Hq, Hkv);
   if (Hq % Hkv != 0)
-    return fail(ATTN_E_ARG, "attn_decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    return fail(ATTN_E_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8)
-    return fail(ATTN_E_UNSUPPORTED, "attn_decode: group size Hq/Hkv=%d not in {1,2,4,8}", G);
-  if (D < 1) return fail(ATTN_E_ARG, "attn_decode: D=%d", D);
+    return fail(ATTN_E_UNSUPPORTED, "%s: group size Hq/Hkv=%d not in {1,2,4,8}", fn, G);
+  if (D < 1) return fail(ATTN_E_ARG, "%s: D=%d", fn, D);
   if (D != 64 && D != 128)
-    return fail(ATTN_E_UNSUPPORTED, "attn_decode: D=%d not in {64,128}", D);
+    return fail(ATTN_E_UNSUPPORTED, "%s: D=%d not in {64,128}", fn, D);
   if (max_length < 1)
-    return fail(ATTN_E_ARG, "attn_decode: max_length=%d must be >= 1", max_length);
+    return fail(ATTN_E_ARG, "%s: max_length=%d must be >= 1", fn, max_length);
   if (!fits({(double)B, (double)Hkv, (double)max_length, (double)D, 4.0}) ||
       !fits({(double)B, (double)Hq, (double)max_length, (double)D, 4.0}))
-    return fail(ATTN_E_ARG, "attn_decode: cache extents overflow");
+    return fail(ATTN_E_ARG, "%s: cache extents overflow", fn);
   if (seq_lens == nullptr && (position_id < 0 || position_id >= max_length))
-    return fail(ATTN_E_ARG, "attn_decode: position_id=%d outside [0, max_length=%d)",
+    return fail(ATTN_E_ARG, "%s: position_id=%d outside [0, max_length=%d)", fn,
                 position_id, max_length);
   if (!std::isfinite(scale) || !(scale > 0.f))
-    return fail(ATTN_E_ARG, "attn_decode: scale must be finite and > 0");
+    return fail(ATTN_E_ARG, "%s: scale must be finite and > 0", fn);
   if (split_rows < 0)
-    return fail(ATTN_E_ARG, "attn_decode: split_rows=%d < 0", split_rows);
+    return fail(ATTN_E_ARG, "%s: split_rows=%d < 0", fn, split_rows);
   if (B == 0) return ok();  // empty batch: nothing is read or written
   if (!q || !k_cache || !v_cache || !out)
-    return fail(ATTN_E_ARG, "attn_decode: null data pointer");
+    return fail(ATTN_E_ARG, "%s: null data pointer", fn);
+  if (k_new && (!v_new || !aligned(k_new, 16) || !aligned(v_new, 16)))
+    return fail(ATTN_E_ARG, "%s: k_new / v_new must be non-null and 16-byte aligned", fn);
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(out, 16))
-    return fail(ATTN_E_ARG, "attn_decode: data pointers must be 16-byte aligned");
+    return fail(ATTN_E_ARG, "%s: data pointers must be 16-byte aligned", fn);
   if (seq_lens && !aligned(seq_lens, 4))
-    return fail(ATTN_E_ARG, "attn_decode: seq_lens must be 4-byte aligned");
+    return fail(ATTN_E_ARG, "%s: seq_lens must be 4-byte aligned", fn);
   const size_t need =
       attn_decode_workspace_bytes(B, Hq, Hkv, D, max_length, split_rows);
   if (workspace == nullptr || workspace_bytes < need)
-    return fail(ATTN_E_WORKSPACE, "attn_decode: workspace %zu bytes, need %zu",
+    return fail(ATTN_E_WORKSPACE, "%s: workspace %zu bytes, need %zu", fn,
                 workspace ? workspace_bytes : (size_t)0, need);
   if (!aligned(workspace, 256))
-    return fail(ATTN_E_WORKSPACE, "attn_decode: workspace must be 256-byte aligned");
+    return fail(ATTN_E_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
 
   const int L_bound = seq_lens ? max_length : position_id + 1;
   attn::DecodeArgs a{};
@@ -209,10 +218,46 @@ int attn_decode(int dtype, const void *q, const void *k_cache,
   a.ws_ml = reinterpret_cast<float *>(ws);
   ws += ws_ml_bytes(B, Hq, a.plan.splits);
   a.ws_o = reinterpret_cast<float *>(ws);
+  if (k_new) {
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_w = const_cast<void *>(k_cache);
+    a.v_w = const_cast<void *>(v_cache);
+  }
   hipError_t e = attn::launch_decode(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "attn_decode launch");
+  if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode(int dtype, const void *q, const void *k_cache,
+                const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
+                int max_length, int position_id, const int32_t *seq_lens,
+                float scale, int split_rows, void *workspace,
+                size_t workspace_bytes, void *stream) {
+  return decode_impl("attn_decode", dtype, q, nullptr, nullptr, k_cache,
+                     v_cache, out, B, Hq, Hkv, D, max_length, position_id,
+                     seq_lens, scale, split_rows, workspace, workspace_bytes,
+                     stream);
+}
+
+int attn_decode_append(int dtype, const void *q, const void *k_new,
+                       const void *v_new, void *k_cache, void *v_cache,
+                       void *out, int B, int Hq, int Hkv, int D, int max_length,
+                       int position_id, const int32_t *seq_lens, float scale,
+                       int split_rows, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  if (B > 0 && (!k_new || !v_new))
+    return fail(ATTN_E_ARG, "attn_decode_append: null k_new / v_new");
+  return decode_impl("attn_decode_append", dtype, q, k_new, v_new, k_cache,
+                     v_cache, out, B, Hq, Hkv, D, max_length, position_id,
+                     seq_lens, scale, split_rows, workspace, workspace_bytes,
+                     stream);
+}
+
 
 int attn_prefill(int dtype, const void *q, const void *k_cache,
                  const void *v_cache, void *out, int B, int Hq, int Hkv, int D,

@@ -212,13 +212,15 @@ struct Bf16Tile {
   static_assert(NOCT * (D / 8) == 64, "one V transpose item per lane");
 };
 
-template <int D, int G>
+template <int D, int G, bool APPEND>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     const uint16_t *__restrict__ qg, const uint16_t *__restrict__ kg,
     const uint16_t *__restrict__ vg, const int32_t *__restrict__ seq_lens,
     int position_id, void *__restrict__ outp, float *__restrict__ ws_ml,
     float *__restrict__ ws_o, int Hq, int Hkv,
-    int max_length, int split_rows, int splits, float qk_scale) {
+    int max_length, int split_rows, int splits, float qk_scale,
+    const uint16_t *__restrict__ knew, const uint16_t *__restrict__ vnew,
+    uint16_t *kw, uint16_t *vw) {
   using T = Bf16Tile<D>;
   constexpr int BN = T::BN, KS = T::KS, NDB = T::NDB, NKB = T::NKB;
   constexpr int SV = T::SV;
@@ -257,6 +259,20 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   const size_t kvbase = ((size_t)b * Hkv + g) * (size_t)max_length * D;
   const uint16_t *kb = kg + kvbase;
   const uint16_t *vb = vg + kvbase;
+  // Appending: the sequence's last valid row is the new token. Its K and V
+  // are read from knew / vnew (so no workgroup reads that cache row while it
+  // is being written) and split 0 stores them into the cache.
+  const int arow = APPEND ? it.L - 1 : -1;
+  const uint16_t *kn = knew + ((size_t)b * Hkv + g) * D;
+  const uint16_t *vn = vnew + ((size_t)b * Hkv + g) * D;
+  if (APPEND && s == 0) {
+    for (int i = tid; i < D / 8; i += kThreads) {
+      *reinterpret_cast<u32x4_t *>(kw + kvbase + (size_t)arow * D + 8 * i) =
+          *reinterpret_cast<const u32x4_t *>(kn + 8 * i);
+      *reinterpret_cast<u32x4_t *>(vw + kvbase + (size_t)arow * D + 8 * i) =
+          *reinterpret_cast<const u32x4_t *>(vn + 8 * i);
+    }
+  }
   uint16_t *vt = reinterpret_cast<uint16_t *>(smem + w * T::VT_BYTES);
   const int oct = l % T::NOCT;  // V transpose item: rows 8*oct..8*oct+7
   const int ch = l / T::NOCT;   //                   dims 8*ch..8*ch+7
@@ -279,14 +295,15 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     for (int kb16 = 0; kb16 < NKB; ++kb16) {
       const int row = min(t0 + kb16 * 16 + li, last_row);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[kb16][ks] = ldnt(kb + (size_t)row * D + ks * 32 + 8 * lg);
+      for (int ks = 0; ks < KS; ++ks)
+        kf[kb16][ks] = ldnt((APPEND && row == arow ? kn : kb + (size_t)row * D) + ks * 32 + 8 * lg);
     }
   };
   auto load_v = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = min(t0 + 8 * oct + i, last_row);
-      vr[i] = ldnt(vb + (size_t)row * D + 8 * ch);
+      vr[i] = ldnt((APPEND && row == arow ? vn : vb + (size_t)row * D) + 8 * ch);
     }
   };
   auto compute_tile = [&](int t0, int tnext) {
@@ -435,13 +452,15 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
 // ---------------------------------------------------------------------------
 // fp32: vector-ALU form
 // ---------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, bool APPEND>
 __global__ __launch_bounds__(kThreads) void decode_f32_kernel(
     const float *__restrict__ qp, const float *__restrict__ kp,
     const float *__restrict__ vp, const int32_t *__restrict__ seq_lens,
     int position_id, void *__restrict__ outp, float *__restrict__ ws_ml,
     float *__restrict__ ws_o, int Hq, int Hkv,
-    int max_length, int split_rows, int splits, float qscale) {
+    int max_length, int split_rows, int splits, float qscale,
+    const float *__restrict__ knew, const float *__restrict__ vnew,
+    float *kw, float *vw) {
   constexpr int VEC = 4;                // floats per 16-byte chunk
   constexpr int LPR = D / VEC;          // lanes per cache row (16 or 32)
   constexpr int NG = kThreads / LPR;    // row groups per workgroup
@@ -484,6 +503,17 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(
   const size_t rowbase = ((size_t)b * Hkv + g) * (size_t)max_length;
   const float *kb = kp + rowbase * D + lr * VEC;
   const float *vb = vp + rowbase * D + lr * VEC;
+  // Appending: as in the bf16 kernel, the last valid row is read from knew /
+  // vnew and split 0 stores it into the cache.
+  const int arow = APPEND ? it.L - 1 : -1;
+  const float *kn = knew + ((size_t)b * Hkv + g) * D + lr * VEC;
+  const float *vn = vnew + ((size_t)b * Hkv + g) * D + lr * VEC;
+  if (APPEND && s == 0 && tid < LPR) {
+    *reinterpret_cast<u32x4_t *>(kw + (rowbase + arow) * D + lr * VEC) =
+        *reinterpret_cast<const u32x4_t *>(kn);
+    *reinterpret_cast<u32x4_t *>(vw + (rowbase + arow) * D + lr * VEC) =
+        *reinterpret_cast<const u32x4_t *>(vn);
+  }
 
   for (int r = it.row0 + grp; r < it.row1; r += NG * U) {
     u32x4_t kr[U], vr[U];
@@ -493,8 +523,8 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(
       kr[u] = u32x4_t{0u, 0u, 0u, 0u};
       vr[u] = kr[u];
       if (rr < it.row1) {
-        kr[u] = ldnt(kb + (size_t)rr * D);
-        vr[u] = ldnt(vb + (size_t)rr * D);
+        kr[u] = ldnt(APPEND && rr == arow ? kn : kb + (size_t)rr * D);
+        vr[u] = ldnt(APPEND && rr == arow ? vn : vb + (size_t)rr * D);
       }
     }
     float sc[U][G];
@@ -676,22 +706,34 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   }
 }
 
-template <bool BF16, int D, int G>
-hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
+template <bool BF16, int D, int G, bool APPEND>
+void launch_split(const DecodeArgs &a, hipStream_t stream) {
   dim3 grid(a.Hkv, a.B, a.plan.splits);
   if constexpr (BF16) {
-    decode_bf16_kernel<D, G><<<grid, kThreads, 0, stream>>>(
+    decode_bf16_kernel<D, G, APPEND><<<grid, kThreads, 0, stream>>>(
         static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
         static_cast<const uint16_t *>(a.v), a.seq_lens, a.position_id, a.out,
         a.ws_ml, a.ws_o, a.Hq, a.Hkv, a.max_length,
-        a.plan.split_rows, a.plan.splits, a.scale * kLog2e);
+        a.plan.split_rows, a.plan.splits, a.scale * kLog2e,
+        static_cast<const uint16_t *>(a.k_new), static_cast<const uint16_t *>(a.v_new),
+        static_cast<uint16_t *>(a.k_w), static_cast<uint16_t *>(a.v_w));
   } else {
-    decode_f32_kernel<D, G><<<grid, kThreads, 0, stream>>>(
+    decode_f32_kernel<D, G, APPEND><<<grid, kThreads, 0, stream>>>(
         static_cast<const float *>(a.q), static_cast<const float *>(a.k),
         static_cast<const float *>(a.v), a.seq_lens, a.position_id, a.out,
         a.ws_ml, a.ws_o, a.Hq, a.Hkv, a.max_length,
-        a.plan.split_rows, a.plan.splits, a.scale * kLog2e);
+        a.plan.split_rows, a.plan.splits, a.scale * kLog2e,
+        static_cast<const float *>(a.k_new), static_cast<const float *>(a.v_new),
+        static_cast<float *>(a.k_w), static_cast<float *>(a.v_w));
   }
+}
+
+template <bool BF16, int D, int G>
+hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
+  if (a.k_new != nullptr)
+    launch_split<BF16, D, G, true>(a, stream);
+  else
+    launch_split<BF16, D, G, false>(a, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.splits <= 1) return e;
   decode_combine_kernel<BF16, D><<<dim3(a.Hq, a.B), 64, 0, stream>>>(

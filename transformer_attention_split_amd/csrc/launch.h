@@ -30,6 +30,11 @@ struct DecodeArgs {
   DecodePlan plan;
   float *ws_ml;  // [B][Hq][splits][2]  (running max, running sum)
   float *ws_o;   // [B][Hq][splits][D]  (unnormalised output)
+  // Fused append (all null for a plain decode): k_new / v_new [B][Hkv][D]
+  // are stored at each sequence's last valid row of the caches k_w / v_w
+  // (the same memory as k / v) and attended to in the same launch.
+  const void *k_new = nullptr, *v_new = nullptr;
+  void *k_w = nullptr, *v_w = nullptr;
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
