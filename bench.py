@@ -380,6 +380,27 @@ def main():
     t_dec = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3
     t_pre = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
     t_tk = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps * 1e-3
+    def back_to_back(fn, n=20):
+        """Per-call time of n consecutive calls between two events (the
+        launch gap after a different kernel is then paid once, not per call)."""
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    t_pre_b2b = back_to_back(lambda: tas.attn_prefill(
+        pre["q"], pre["k"], pre["v"], prefix_len=pp["prefix_len"],
+        scale=pp["scale"], out=pre["out"]))
+    t_tk_b2b = back_to_back(lambda: tas.attn_topk(
+        tk["q"], tk["k"], tk["v"], tk["p"]["topk"], out=tk["out"]))
+
     def pct(i):
         xs = np.array([e[i].elapsed_time(e[i + 1]) * 1e3 for e in evs])
         return {k: round(float(np.percentile(xs, q)), 2)
@@ -397,11 +418,16 @@ def main():
                         TFLOPs=round(pre_tflops, 2),
                         frac_of_bf16_mfma_peak=round(
                             pre_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                        flops=pre["flops"], us_percentiles=pre_pct),
+                        flops=pre["flops"], us_percentiles=pre_pct,
+                        us_back_to_back=round(t_pre_b2b, 2),
+                        TFLOPs_back_to_back=round(pre["flops"] / t_pre_b2b / 1e6, 2),
+                        frac_back_to_back=round(pre["flops"] / t_pre_b2b / 1e6
+                                                / BF16_MFMA_PEAK_TFLOPS, 4)),
         "topk": dict(workload="topk_c2psa", us=round(t_tk * 1e6, 2),
                      TFLOPs=round(tk_tflops, 3),
                      frac_of_fp64_peak=round(tk_tflops / FP64_PEAK_TFLOPS, 4),
-                     flops=tk["flops"], us_percentiles=tk_pct),
+                     flops=tk["flops"], us_percentiles=tk_pct,
+                     us_back_to_back=round(t_tk_b2b, 2)),
     }
     if not args.no_secondary:
         log("fused append + decode on the ragged batch ...")
