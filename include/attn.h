@@ -192,7 +192,8 @@ int attn_prefill(int dtype, const void *q, const void *k_cache,
  *                 indices of each row in ascending order.
  * Supported: d == 64; 1 <= n <= 1024; 1 <= topk <= n; b, h <= 65535 and
  * b·h·ceil(n/16) <= 2^23 (one workgroup per 16 rows). b == 0 or h == 0 is a
- * no-op. */
+ * no-op. Inputs must be finite (a NaN or infinite input leaves the
+ * selection unspecified). */
 int attn_topk(const float *q, const float *k, const float *v, float *out,
               int32_t *idx_out, int b, int h, int n, int d, int topk,
               void *stream);

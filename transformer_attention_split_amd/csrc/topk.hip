@@ -14,15 +14,16 @@
 //      B = 16 key rows per block; the 64 dimensions are spread as 16 MFMAs of
 //      4), written to LDS. Waves take key blocks round-robin.
 //   2. select, one row per wave at a time, lane e holding keys e, e+64, ...:
-//      a) the k-th largest fp32-rounded score T by a most-significant-digit
-//         radix select over the 32-bit order-preserving key: four passes of
-//         8 bits, each a 256-bin LDS histogram of the keys still sharing the
-//         prefix, a wave prefix sum over the bins from the top and a ballot
-//         for the bin holding the k-th key. Every score whose fp32 key
-//         exceeds T is in (rounding is monotone);
-//      b) only if more scores share T than places remain, a bisection over
-//         the exact 64-bit keys of those candidates, and remaining ties are
-//         filled in ascending key index.
+//      a) the row's score range (fp32-rounded, wave-wide max/min over DPP
+//         and permlane swaps) defines a monotone map of the scores onto 256
+//         buckets; a 256-bin LDS histogram scanned from the top gives the
+//         bucket B holding the topk-th largest score: every score in a higher
+//         bucket is taken;
+//      b) the candidates in B are ranked exactly (fp64 score descending, key
+//         index ascending) against each other with lane reads, and the first
+//         topk - (scores above B) are taken; if more than 64 scores share B
+//         (equal or nearly equal scores), a bisection over their exact 64-bit
+//         order keys decides instead, remaining ties in ascending key index.
 //      The chosen (index, score) pairs are compacted in ascending index order
 //      (into the row's own LDS storage and a per-wave index list).
 //   3. gather: lanes = 4 slot groups x 16 groups of 4 dimensions; each slot
@@ -70,6 +71,26 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Maximum / minimum over the 64 lanes without LDS round trips: DPP moves
+// inside each 16-lane row (swap neighbours, swap pairs, mirror the 8-lane
+// halves, mirror the row), then v_permlane16_swap / v_permlane32_swap across
+// rows.
+template <bool MAX>
+__device__ __forceinline__ float wave_extreme(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+#define ATTN_DPP(v, ctrl) \
+  __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false))
+  x = op(x, ATTN_DPP(x, 0xB1));   // quad_perm [1,0,3,2]
+  x = op(x, ATTN_DPP(x, 0x4E));   // quad_perm [2,3,0,1]
+  x = op(x, ATTN_DPP(x, 0x141));  // row_half_mirror
+  x = op(x, ATTN_DPP(x, 0x140));  // row_mirror
+#undef ATTN_DPP
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ uint64_t order64(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
@@ -85,6 +106,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   double *S = reinterpret_cast<double *>(smem);                 // [QB][NP]
   int *jl = reinterpret_cast<int *>(smem + (size_t)QB * NP * 8);  // [4][NP]
   __shared__ __attribute__((aligned(16))) uint32_t hst[4 * 256];  // per-wave histograms
+  __shared__ double cand_s[4 * 64];  // per-wave boundary candidates (score,
+  __shared__ int cand_j[4 * 64];     // key index)
   for (int i = threadIdx.x; i < 4 * 256; i += kThreads) hst[i] = 0u;
 
   // Workgroup i runs on XCD i % 8. Each XCD takes a contiguous range of the
@@ -178,70 +201,113 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     if (row_ok) {
       // ---- 2. select ---------------------------------------------------------------
       double s[NTP];
-      uint32_t k32[NTP];
+      bool ok[NTP];
+      float mxf = -__builtin_inff(), mnf = __builtin_inff();
 #pragma unroll
       for (int t = 0; t < NTP; ++t) {
-        // computed for every slot (padding too: in bounds, maybe stale) and
-        // then selected, so that no load waits behind a branch
-        const double v = S[i * NP + l + 64 * t] + 0.0;  // +0.0 turns -0 into +0
-        const uint32_t key = order32((float)v + 0.0f);
-        const bool ok = l + 64 * t < n;
-        s[t] = ok ? v : 0.0;
-        k32[t] = ok ? key : 0u;
+        // read for every slot (padding too: in bounds, maybe stale) and then
+        // selected, so that no load waits behind a branch
+        s[t] = S[i * NP + l + 64 * t] + 0.0;  // +0.0 turns -0 into +0
+        ok[t] = l + 64 * t < n;
+        mxf = fmaxf(mxf, ok[t] ? (float)s[t] : -__builtin_inff());
+        mnf = fminf(mnf, ok[t] ? (float)s[t] : __builtin_inff());
       }
-      // k-th largest 32-bit key by 4 radix passes of 8 bits, most
-      // significant first: histogram the candidates' digit in LDS, scan
-      // the bins from the top, keep the bin that holds the k-th key.
-      uint32_t T = 0;        // key prefix found so far
-      int krem = topk;       // rank still to find inside the prefix
-      int gt = 0;            // keys above the prefix
-      int nc = 0;            // keys equal to the final key
+      // (fp32-rounded range: any constants give a monotone map below)
+      const double mx = wave_extreme<true>(mxf), mn = wave_extreme<false>(mnf);
+      // Bucket of a score: a non-decreasing map of about [mn, mx] onto
+      // 0..255 (correctly rounded fma, truncation and clamping are all
+      // monotone), so a higher bucket means a strictly larger score. Equal
+      // scores share a bucket; a row of (nearly) equal scores is all bucket 0.
+      const double span = mx - mn;
+      const double bs = span > 1e-290 ? 256.0 / span : 0.0;
+      const double b0 = -mn * bs;
+      int bk[NTP];
+#pragma unroll
+      for (int t = 0; t < NTP; ++t) {
+        const int bb = (int)fma(s[t], bs, b0);
+        bk[t] = ok[t] ? min(max(bb, 0), 255) : -1;
+      }
+      // 256-bin histogram, scanned from the top: bucket B holds the topk-th
+      // largest score, gt scores lie in higher buckets, nc in B.
       uint32_t *hist = hst + w * 256;
 #pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-#pragma unroll
-        for (int t = 0; t < NTP; ++t) {
-          const bool cand = k32[t] != 0u &&
-                            (pass == 0 || (k32[t] >> (shift + 8)) == T);
-          if (cand) atomicAdd(&hist[(k32[t] >> shift) & 0xffu], 1u);
-        }
-        wave_sync();
+      for (int t = 0; t < NTP; ++t)
+        if (bk[t] >= 0) atomicAdd(&hist[bk[t]], 1u);
+      wave_sync();
+      int B, gt, nc;
+      {
         // lane l holds bins 255-4l (top) .. 252-4l
         const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(&hist[252 - 4 * l]);
         const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
         const uint32_t incl = wave_inclusive_scan(local, l);
-        const uint64_t hit = __ballot(incl >= (uint32_t)krem);
+        const uint64_t hit = __ballot(incl >= (uint32_t)topk);
         const int L = __ffsll((unsigned long long)hit) - 1;
         uint32_t c = __builtin_amdgcn_readlane(incl - local, L);
         const uint32_t h3 = __builtin_amdgcn_readlane(hv[3], L);
         const uint32_t h2 = __builtin_amdgcn_readlane(hv[2], L);
         const uint32_t h1 = __builtin_amdgcn_readlane(hv[1], L);
         const uint32_t h0 = __builtin_amdgcn_readlane(hv[0], L);
-        int bin, hb;
-        if (c + h3 >= (uint32_t)krem) { bin = 255 - 4 * L; hb = h3; }
-        else if ((c += h3) + h2 >= (uint32_t)krem) { bin = 254 - 4 * L; hb = h2; }
-        else if ((c += h2) + h1 >= (uint32_t)krem) { bin = 253 - 4 * L; hb = h1; }
-        else { c += h1; bin = 252 - 4 * L; hb = h0; }
-        krem -= (int)c;
-        gt += (int)c;
-        T = (T << 8) | (uint32_t)bin;
+        int hb;
+        if (c + h3 >= (uint32_t)topk) { B = 255 - 4 * L; hb = h3; }
+        else if ((c += h3) + h2 >= (uint32_t)topk) { B = 254 - 4 * L; hb = h2; }
+        else if ((c += h2) + h1 >= (uint32_t)topk) { B = 253 - 4 * L; hb = h1; }
+        else { c += h1; B = 252 - 4 * L; hb = h0; }
+        gt = (int)c;
         nc = hb;
         *reinterpret_cast<u32x4_t *>(&hist[252 - 4 * l]) = u32x4_t{0u, 0u, 0u, 0u};
-        wave_sync();
       }
       uint64_t selm[NTP], cm[NTP];
 #pragma unroll
       for (int t = 0; t < NTP; ++t) {
-        selm[t] = __ballot(k32[t] > T);
-        cm[t] = __ballot(k32[t] == T);
+        selm[t] = __ballot(bk[t] > B);
+        cm[t] = __ballot(bk[t] == B);
       }
-      const int need = topk - gt;  // >= 1
+      const int need = topk - gt;  // 1 <= need <= nc
       if (nc == need) {
 #pragma unroll
         for (int t = 0; t < NTP; ++t) selm[t] |= cm[t];
+      } else if (nc <= 64) {
+        // The boundary bucket's candidates go to a per-wave list; each is
+        // ranked by (score descending, index ascending) and the candidate of
+        // rank need-1 is the last one taken.
+        double *cs = cand_s + w * 64;
+        int *cj = cand_j + w * 64;
+        int before = 0;
+#pragma unroll
+        for (int t = 0; t < NTP; ++t) {
+          if ((cm[t] >> l) & 1ull) {
+            const int pos = before + __popcll(cm[t] & below);
+            cs[pos] = s[t];
+            cj[pos] = l + 64 * t;
+          }
+          before += __popcll(cm[t]);
+        }
+        wave_sync();
+        const double my_s = cs[l < nc ? l : 0];
+        const int my_j = cj[l < nc ? l : 0];
+        // candidate m is in lane m: broadcast it with lane reads
+        const int my_lo = (int)(uint32_t)__double_as_longlong(my_s);
+        const int my_hi = (int)(uint32_t)(__double_as_longlong(my_s) >> 32);
+        int rank = 0;
+        for (int m = 0; m < nc; ++m) {
+          const uint64_t ob = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(my_hi, m) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane(my_lo, m);
+          const double os = __longlong_as_double((long long)ob);
+          const int oj = __builtin_amdgcn_readlane(my_j, m);
+          rank += (os > my_s || (os == my_s && oj < my_j)) ? 1 : 0;
+        }
+        const uint64_t last = __ballot(l < nc && rank == need - 1);
+        const int Ll = __ffsll((unsigned long long)last) - 1;
+        const double ts = __shfl(my_s, Ll);
+        const int tj = __shfl(my_j, Ll);
+#pragma unroll
+        for (int t = 0; t < NTP; ++t)
+          selm[t] |= __ballot(((cm[t] >> l) & 1ull) &&
+                              (s[t] > ts || (s[t] == ts && l + 64 * t <= tj)));
+        wave_sync();
       } else {
-        // Exact fp64 order among the candidates sharing the fp32 key T.
+        // Many equal or nearly equal scores: exact fp64 order among the
+        // candidates by a bisection over their 64-bit order keys.
         uint64_t k64[NTP];
 #pragma unroll
         for (int t = 0; t < NTP; ++t)
