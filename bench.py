@@ -236,6 +236,51 @@ def bench_append(torch, tas, dec, steps):
                 GBps_append_decode=round(dec["bytes"] / (ta * 1e-6) / 1e9, 1))
 
 
+def bench_paged(torch, tas, dec, steps, page_size, layout):
+    """attn_decode_paged on the ragged batch cut into pages of `page_size`
+    rows (token- or head-major) in a shuffled order, built on the device from
+    the contiguous cache, against attn_decode on the contiguous cache."""
+    import numpy as np
+    p = dec["p"]
+    B, Hkv, D, M = p["B"], p["Hkv"], p["D"], p["max_length"]
+    nb = M // page_size
+    g = torch.Generator(device="cpu").manual_seed(4321)
+    perm = torch.randperm(B * nb, generator=g).to(torch.int32)
+    table = perm.view(B, nb).cuda()
+    perm_dims = (0, 2, 3, 1, 4) if layout == "token" else (0, 2, 1, 3, 4)
+    src_k = dec["k"].view(B, Hkv, nb, page_size, D).permute(*perm_dims)
+    src_v = dec["v"].view(B, Hkv, nb, page_size, D).permute(*perm_dims)
+    kp = torch.empty((B * nb,) + tuple(src_k.shape[2:]), dtype=torch.bfloat16,
+                     device="cuda")
+    vp = torch.empty_like(kp)
+    idx = table.view(-1).long()
+    kp[idx] = src_k.reshape(kp.shape)
+    vp[idx] = src_v.reshape(vp.shape)
+    out = torch.empty_like(dec["out"])
+    kw = dict(seq_lens=dec["seq_lens"], scale=p["scale"], out=out,
+              workspace=dec["ws"])
+    for _ in range(5):
+        tas.attn_decode_paged(dec["q"], kp, vp, table, layout=layout, **kw)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+          for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        tas.attn_decode_paged(dec["q"], kp, vp, table, layout=layout, **kw)
+        e[1].record()
+        tas.attn_decode(dec["q"], dec["k"], dec["v"], **kw)
+        e[2].record()
+    torch.cuda.synchronize()
+    tp = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in ev]))
+    td = float(np.median([e[1].elapsed_time(e[2]) * 1e3 for e in ev]))
+    del kp, vp
+    torch.cuda.empty_cache()
+    return dict(workload=f"decode_ragged_b64 in shuffled {page_size}-row "
+                         f"{layout}-major pages",
+                us_p50_paged=round(tp, 2), us_p50_contiguous=round(td, 2),
+                GBps_paged=round(dec["bytes"] / (tp * 1e-6) / 1e9, 1))
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the decode workload
 # ----------------------------------------------------------------------------
@@ -433,6 +478,10 @@ def main():
         log("fused append + decode on the ragged batch ...")
         secondary["decode_append_ragged_b64"] = bench_append(torch, tas, dec,
                                                              args.steps)
+        log("paged decode on the ragged batch ...")
+        secondary["decode_paged_ragged_b64"] = [
+            bench_paged(torch, tas, dec, args.steps, ps, lay)
+            for lay in ("token", "head") for ps in (64, 256)]
     if not args.no_secondary:
         log("single-sequence position-8000 decode (graph replay) ...")
         secondary["decode_single_pos8000"] = bench_single_position(

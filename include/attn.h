@@ -1,8 +1,9 @@
 /*
  * attn.h — C ABI of the MI355X (gfx950) KV-cache attention library.
  *
- * Three operations (plus decode with a fused cache append), each one
- * asynchronous launch sequence on the caller's HIP stream:
+ * Three operations (plus decode with a fused cache append and decode over a
+ * paged cache), each one asynchronous launch sequence on the caller's HIP
+ * stream:
  *
  *   attn_decode   single-token decode over a statically preallocated cache,
  *                 attending to rows [0, position_id] (or [0, seq_lens[b]) for
@@ -150,6 +151,50 @@ int attn_decode_append(int dtype, const void *q, const void *k_new,
                        int position_id, const int32_t *seq_lens, float scale,
                        int split_rows, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/* Page layouts of attn_decode_paged. */
+typedef enum attn_page_layout {
+  ATTN_PAGES_TOKEN_MAJOR = 0, /* page [page_size][Hkv][D]                  */
+  ATTN_PAGES_HEAD_MAJOR = 1   /* page [Hkv][page_size][D]                  */
+} attn_page_layout;
+
+/* Decode over a paged KV cache. The cache of a sequence is a list of pages
+ * (the block-table indirection of paged serving caches). Within a page the
+ * rows are token-major, as the prefix cache of "step14_3 — batched attention:
+ * removing the per-head Python loop" (problem section) stores K and V with
+ * the head after the token, or head-major (each head's rows contiguous, which
+ * streams like the static cache). The result equals attn_decode on the
+ * contiguous cache gathered from the pages.
+ *
+ *   dtype        ATTN_BF16 only.
+ *   k_pages,
+ *   v_pages      ATTN_PAGES_TOKEN_MAJOR: [num_pages][page_size][Hkv][D], row r
+ *                of kv head g of sequence b is k_pages[block_table[b][r /
+ *                page_size]][r % page_size][g][:]; ATTN_PAGES_HEAD_MAJOR:
+ *                [num_pages][Hkv][page_size][D], the same row is
+ *                k_pages[...][g][r % page_size][:]. Pages a sequence does not
+ *                reach are never read; rows past its length in its last page
+ *                may hold anything.
+ *   page_layout  ATTN_PAGES_TOKEN_MAJOR or ATTN_PAGES_HEAD_MAJOR.
+ *   block_table  DEVICE int32 [B][max_blocks]; entries are clamped to
+ *                [0, num_pages) on the device (so a bad entry reads a wrong
+ *                page, never outside the pages).
+ *   position_id, seq_lens, scale, split_rows, workspace, q, out: as for
+ *                attn_decode with max_length = max_blocks * page_size (the
+ *                workspace size is attn_decode_workspace_bytes(B, Hq, Hkv, D,
+ *                max_blocks * page_size, split_rows)). split_rows is rounded up
+ *                to a multiple of the kernel's wave tile (4096 / D rows).
+ * Supported: D in {64, 128}; page_size a multiple of 4096 / D (32 rows at
+ * D = 128, 64 at D = 64) up to 65536; Hq/Hkv in {1, 2, 4, 8}; B, Hkv <=
+ * 65535; max_blocks * page_size < 2^31. ATTN_E_ARG for page_size, max_blocks
+ * or num_pages < 1, an unknown page_layout or a null block_table with B > 0. */
+int attn_decode_paged(int dtype, const void *q, const void *k_pages,
+                      const void *v_pages, const int32_t *block_table,
+                      int max_blocks, int page_size, int num_pages,
+                      int page_layout, void *out,
+                      int B, int Hq, int Hkv, int D, int position_id,
+                      const int32_t *seq_lens, float scale, int split_rows,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* --------------------------------------------------------------------------
  * Prefill

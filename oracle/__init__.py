@@ -8,6 +8,7 @@ from .attention import (  # noqa: F401
     default_scale,
     decode,
     decode_append,
+    decode_paged,
     decode_sequence,
     prefill,
     topk_sparse,

@@ -137,6 +137,43 @@ def decode_append(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
     return out, k2, v2
 
 
+def decode_paged(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray,
+                 block_table: np.ndarray,
+                 position_id: Optional[int] = None,
+                 seq_lens: Optional[np.ndarray] = None,
+                 scale: Optional[float] = None,
+                 layout: str = "token") -> np.ndarray:
+    """Decode over a paged cache: pages [num_pages, page_size, Hkv, D] hold
+    rows token-major (the head after the token, as the prefix cache of
+    [P2, problem section] stores K and V), or [num_pages, Hkv, page_size, D]
+    head-major; row r of sequence b is row r % page_size of page
+    block_table[b, r // page_size] (reading: the block-table indirection is
+    not spelled out on the pages). The logical cache is gathered row by row
+    and attended to as in ``decode``; page indices are clamped to the pages
+    that exist, as the library does.
+    """
+    if layout == "token":
+        num_pages, page_size, Hkv, D = k_pages.shape
+    else:
+        num_pages, Hkv, page_size, D = k_pages.shape
+    B, max_blocks = block_table.shape
+    M = max_blocks * page_size
+    k = np.empty((B, Hkv, M, D), dtype=k_pages.dtype)
+    v = np.empty((B, Hkv, M, D), dtype=v_pages.dtype)
+    for b in range(B):
+        for r in range(M):
+            pg = int(min(max(int(block_table[b, r // page_size]), 0),
+                         num_pages - 1))
+            if layout == "token":
+                k[b, :, r, :] = k_pages[pg, r % page_size]
+                v[b, :, r, :] = v_pages[pg, r % page_size]
+            else:
+                k[b, :, r, :] = k_pages[pg, :, r % page_size]
+                v[b, :, r, :] = v_pages[pg, :, r % page_size]
+    return decode(q, k, v, position_id=position_id, seq_lens=seq_lens,
+                  scale=scale)
+
+
 # ----------------------------------------------------------------------------
 # Causal prefill against a cached prefix  [P2 solution section]
 # ----------------------------------------------------------------------------

@@ -161,6 +161,36 @@ def new_token_kv(seed: int, B: int, Hkv: int, D: int, dtype: str):
     return _draw(rng, (B, Hkv, D), dtype), _draw(rng, (B, Hkv, D), dtype)
 
 
+def paginate(k_cache: np.ndarray, v_cache: np.ndarray, page_size: int,
+             seed: int, extra_pages: int = 3, dtype: str = "bf16",
+             layout: str = "token"):
+    """Scatter a contiguous cache [B, Hkv, M, D] (M a multiple of page_size)
+    into pages in a seeded random order, token-major [num_pages, page_size,
+    Hkv, D] or head-major [num_pages, Hkv, page_size, D], with `extra_pages`
+    unreferenced pages filled with NaN. Returns (k_pages, v_pages,
+    block_table int32 [B, M / page_size])."""
+    B, Hkv, M, D = k_cache.shape
+    assert M % page_size == 0
+    nb = M // page_size
+    num_pages = B * nb + extra_pages
+    rng = np.random.default_rng([seed, 7])
+    perm = rng.permutation(num_pages)
+    table = perm[:B * nb].reshape(B, nb).astype(np.int32)
+    shape = ((num_pages, page_size, Hkv, D) if layout == "token"
+             else (num_pages, Hkv, page_size, D))
+    kp = np.full(shape, _nan_of(dtype), k_cache.dtype)
+    vp = np.full(shape, _nan_of(dtype), v_cache.dtype)
+    for b in range(B):
+        for blk in range(nb):
+            rows = slice(blk * page_size, (blk + 1) * page_size)
+            kb, vb = k_cache[b, :, rows, :], v_cache[b, :, rows, :]
+            if layout == "token":
+                kb, vb = kb.transpose(1, 0, 2), vb.transpose(1, 0, 2)
+            kp[table[b, blk]] = kb
+            vp[table[b, blk]] = vb
+    return kp, vp, table
+
+
 # ----------------------------------------------------------------------------
 # Prefill inputs
 # ----------------------------------------------------------------------------

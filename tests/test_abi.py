@@ -139,6 +139,51 @@ def test_decode_append_batch_zero_is_a_noop():
     assert decode_append(B=0, kn=None, vn=None, ws=None, ws_bytes=0) == OK
 
 
+def decode_paged(**kw):
+    a = dict(dtype=BF16, q=P, kp=P, vp=P, bt=P, max_blocks=64, page_size=128,
+             num_pages=100, layout=0, out=P, B=1, Hq=32, Hkv=8, D=128,
+             position_id=100,
+             seq_lens=None, scale=0.088, split_rows=0, ws=P, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.attn_decode_paged(a["dtype"], a["q"], a["kp"], a["vp"], a["bt"],
+                                 a["max_blocks"], a["page_size"],
+                                 a["num_pages"], a["layout"], a["out"],
+                                 a["B"], a["Hq"],
+                                 a["Hkv"], a["D"], a["position_id"],
+                                 a["seq_lens"], a["scale"], a["split_rows"],
+                                 a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=F32), E_UNSUP),
+    (dict(dtype=5), E_ARG),
+    (dict(D=96), E_UNSUP),
+    (dict(page_size=0), E_ARG),
+    (dict(page_size=48), E_UNSUP),           # not a multiple of 32 at D=128
+    (dict(D=64, page_size=32), E_UNSUP),     # not a multiple of 64 at D=64
+    (dict(page_size=1 << 17), E_UNSUP),
+    (dict(max_blocks=0), E_ARG),
+    (dict(num_pages=0), E_ARG),
+    (dict(layout=2), E_ARG),
+    (dict(layout=-1), E_ARG),
+    (dict(bt=None), E_ARG),
+    (dict(bt=P + 2), E_ARG),
+    (dict(position_id=64 * 128), E_ARG),    # past max_blocks * page_size
+    (dict(max_blocks=1 << 20, page_size=4096), E_ARG),
+    (dict(kp=None), E_ARG),
+    (dict(Hq=24), E_UNSUP),
+    (dict(ws=None), E_WS),
+])
+def test_decode_paged_rejects(kw, status):
+    assert decode_paged(**kw) == status
+    assert lib.attn_last_error().decode().startswith("attn_decode_paged")
+
+
+def test_decode_paged_batch_zero_is_a_noop():
+    assert decode_paged(B=0, bt=None, ws=None, ws_bytes=0) == OK
+
+
 def test_decode_workspace_bound():
     ws = lib.attn_decode_workspace_bytes
     assert ws(0, 32, 8, 128, 8192, 0) == 0

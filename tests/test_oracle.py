@@ -197,6 +197,41 @@ def test_decode_append_ragged_rows_and_empty_sequence():
                                rtol=0, atol=1e-15)
 
 
+def test_decode_paged_equals_contiguous_and_sdpa():
+    # a contiguous cache scattered over shuffled token-major pages (spare
+    # pages hold NaN): the paged oracle must see exactly the same rows
+    rng = np.random.default_rng(91)
+    B, Hq, Hkv, D, M, ps = 3, 4, 2, 8, 24, 8
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, M, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, M, D)).astype(np.float32)
+    kp, vp, table = synth.paginate(k, v, ps, seed=91, dtype="f32")
+    assert len(set(table.ravel().tolist())) == B * M // ps
+    lens = np.array([M, 1, 13])
+    out = oracle.decode_paged(q, kp, vp, table, seq_lens=lens)
+    np.testing.assert_array_equal(out, oracle.decode(q, k, v, seq_lens=lens))
+    # head-major pages hold the same rows: kp_h[p, g, r] == kp[p, r, g]
+    kh, vh, th = synth.paginate(k, v, ps, seed=91, dtype="f32", layout="head")
+    np.testing.assert_array_equal(th, table)
+    np.testing.assert_array_equal(kh, kp.transpose(0, 2, 1, 3))
+    np.testing.assert_array_equal(
+        oracle.decode_paged(q, kh, vh, th, seq_lens=lens, layout="head"), out)
+    for b in range(B):
+        ref = _sdpa_sliced(q[b:b + 1], k[b:b + 1], v[b:b + 1], int(lens[b]))
+        np.testing.assert_allclose(out[b:b + 1], ref, rtol=0, atol=1e-12)
+    # the page of row r is table[b, r // ps]: swapping two table entries of
+    # a sequence swaps those blocks of rows
+    t2 = table.copy()
+    t2[0, [0, 2]] = t2[0, [2, 0]]
+    k2 = k.copy()
+    k2[0, :, 0:8], k2[0, :, 16:24] = k[0, :, 16:24], k[0, :, 0:8]
+    v2 = v.copy()
+    v2[0, :, 0:8], v2[0, :, 16:24] = v[0, :, 16:24], v[0, :, 0:8]
+    np.testing.assert_array_equal(
+        oracle.decode_paged(q, kp, vp, t2, position_id=M - 1),
+        oracle.decode(q, k2, v2, position_id=M - 1))
+
+
 def test_decode_sliced_equals_masked_full_cache():
     # The page's original form: full cache, bool mask arange(max) <= pos.
     rng = np.random.default_rng(2)

@@ -16,11 +16,13 @@ from ._binding import (  # noqa: F401
     AttnError,
     attn_decode,
     attn_decode_append,
+    attn_decode_paged,
     attn_decode_workspace_bytes,
     attn_prefill,
     attn_topk,
     lib,
 )
 
-__all__ = ["attn_decode", "attn_decode_append", "attn_prefill", "attn_topk",
+__all__ = ["attn_decode", "attn_decode_append", "attn_decode_paged",
+           "attn_prefill", "attn_topk",
            "attn_decode_workspace_bytes", "AttnError", "AttnArgError"]

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libattn.so")
 
 ATTN_OK, ATTN_E_ARG, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = range(5)
 ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_PAGES_TOKEN_MAJOR, ATTN_PAGES_HEAD_MAJOR = 0, 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -47,6 +48,9 @@ lib.attn_decode.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p,
 lib.attn_decode_append.restype = _i
 lib.attn_decode_append.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i,
                                    _i, _i, _p, _f, _i, _p, _sz, _p]
+lib.attn_decode_paged.restype = _i
+lib.attn_decode_paged.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _i,
+                                  _i, _i, _i, _i, _p, _f, _i, _p, _sz, _p]
 lib.attn_prefill.restype = _i
 lib.attn_prefill.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
                              _f, _p]
@@ -55,7 +59,7 @@ lib.attn_topk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 
 EXPORTED = ("attn_status_str", "attn_last_error", "attn_abi_version",
             "attn_decode_workspace_bytes", "attn_decode", "attn_decode_append",
-            "attn_prefill", "attn_topk")
+            "attn_decode_paged", "attn_prefill", "attn_topk")
 
 
 class AttnError(RuntimeError):
@@ -201,6 +205,71 @@ def attn_decode_append(q: torch.Tensor, k_new: torch.Tensor,
         scale, int(split_rows), _ptr(workspace), workspace.numel(),
         _stream_handle(stream))
     _check(st, "attn_decode_append")
+    return out
+
+
+def attn_decode_paged(q: torch.Tensor, k_pages: torch.Tensor,
+                      v_pages: torch.Tensor, block_table: torch.Tensor, *,
+                      layout: str = "token",
+                      position_id: Optional[int] = None,
+                      seq_lens: Optional[torch.Tensor] = None,
+                      scale: Optional[float] = None, split_rows: int = 0,
+                      out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Decode over a paged cache. q [B,Hq,D] bf16; pages
+    [num_pages,page_size,Hkv,D] (layout="token") or [num_pages,Hkv,page_size,D]
+    (layout="head"); block_table int32 [B,max_blocks] on the GPU; exactly one
+    of position_id or seq_lens. Returns out [B,Hq,D]."""
+    _need_dense("q", q, 3)
+    _need_dense("k_pages", k_pages, 4)
+    _need_dense("v_pages", v_pages, 4)
+    _need_dense("block_table", block_table, 2)
+    if k_pages.shape != v_pages.shape:
+        raise ValueError("k_pages and v_pages shapes differ")
+    if not (q.dtype == k_pages.dtype == v_pages.dtype):
+        raise ValueError("q, k_pages and v_pages must share one dtype")
+    if block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32")
+    B, Hq, D = q.shape
+    if layout == "token":
+        num_pages, page_size, Hkv, Dk = k_pages.shape
+        code = ATTN_PAGES_TOKEN_MAJOR
+    elif layout == "head":
+        num_pages, Hkv, page_size, Dk = k_pages.shape
+        code = ATTN_PAGES_HEAD_MAJOR
+    else:
+        raise ValueError("layout must be 'token' or 'head'")
+    if Dk != D or block_table.shape[0] != B:
+        raise ValueError("page, block-table and query shapes do not match")
+    max_blocks = block_table.shape[1]
+    if (position_id is None) == (seq_lens is None):
+        raise ValueError("pass exactly one of position_id or seq_lens")
+    if seq_lens is not None:
+        _need_dense("seq_lens", seq_lens, 1)
+        if seq_lens.dtype != torch.int32 or seq_lens.numel() != B:
+            raise ValueError("seq_lens must be int32 [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_dense("out", out, 3)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q's shape and dtype")
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, D, max_blocks * page_size,
+                                       split_rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8,
+                                device=q.device)
+    st = lib.attn_decode_paged(
+        _dtype_code(q), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+        _ptr(block_table), max_blocks, page_size, num_pages, code, _ptr(out),
+        B, Hq,
+        Hkv, D, -1 if position_id is None else int(position_id),
+        _ptr(seq_lens), float(scale), int(split_rows), _ptr(workspace),
+        workspace.numel(), _stream_handle(stream))
+    _check(st, "attn_decode_paged")
     return out
 
 

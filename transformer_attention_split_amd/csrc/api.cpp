@@ -146,14 +146,17 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D,
 
 namespace {
 
-// Checks and launch shared by attn_decode and attn_decode_append (fn names
-// the entry point in error messages; k_new == nullptr: plain decode).
-int decode_impl(const char *fn, int dtype, const void *q, const void *k_new,
-                const void *v_new, const void *k_cache, const void *v_cache,
-                void *out, int B, int Hq, int Hkv, int D, int max_length,
-                int position_id, const int32_t *seq_lens, float scale,
-                int split_rows, void *workspace, size_t workspace_bytes,
-                void *stream) {
+// Checks shared by the decode entry points (fn names the entry point in error
+// messages; k_new == nullptr: no append) and the launch arguments they imply;
+// split lengths are rounded up to a multiple of row_multiple. Returns ATTN_OK
+// with a.B == 0 for an empty batch (nothing to launch).
+int decode_check(const char *fn, int dtype, const void *q, const void *k_new,
+                 const void *v_new, const void *k_cache, const void *v_cache,
+                 void *out, int B, int Hq, int Hkv, int D, int max_length,
+                 int position_id, const int32_t *seq_lens, float scale,
+                 int split_rows, void *workspace, size_t workspace_bytes,
+                 int row_multiple, attn::DecodeArgs &a) {
+  a = attn::DecodeArgs{};
   if (dtype != ATTN_F32 && dtype != ATTN_BF16)
     return fail(ATTN_E_ARG, "%s: unknown dtype %d", fn, dtype);
   if (B < 0 || B > 65535)
@@ -199,7 +202,6 @@ int decode_impl(const char *fn, int dtype, const void *q, const void *k_new,
     return fail(ATTN_E_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
 
   const int L_bound = seq_lens ? max_length : position_id + 1;
-  attn::DecodeArgs a{};
   a.bf16 = dtype == ATTN_BF16;
   a.q = q;
   a.k = k_cache;
@@ -214,6 +216,10 @@ int decode_impl(const char *fn, int dtype, const void *q, const void *k_new,
   a.seq_lens = seq_lens;
   a.scale = scale;
   a.plan = plan_decode(B, Hkv, D, max_length, L_bound, split_rows);
+  if (a.plan.split_rows % row_multiple != 0) {  // fewer splits: still fits
+    a.plan.split_rows = ceil_div(a.plan.split_rows, row_multiple) * row_multiple;
+    a.plan.splits = ceil_div(L_bound, a.plan.split_rows);
+  }
   char *ws = static_cast<char *>(workspace);
   a.ws_ml = reinterpret_cast<float *>(ws);
   ws += ws_ml_bytes(B, Hq, a.plan.splits);
@@ -224,6 +230,21 @@ int decode_impl(const char *fn, int dtype, const void *q, const void *k_new,
     a.k_w = const_cast<void *>(k_cache);
     a.v_w = const_cast<void *>(v_cache);
   }
+  return ok();
+}
+
+int decode_impl(const char *fn, int dtype, const void *q, const void *k_new,
+                const void *v_new, const void *k_cache, const void *v_cache,
+                void *out, int B, int Hq, int Hkv, int D, int max_length,
+                int position_id, const int32_t *seq_lens, float scale,
+                int split_rows, void *workspace, size_t workspace_bytes,
+                void *stream) {
+  attn::DecodeArgs a;
+  const int st = decode_check(fn, dtype, q, k_new, v_new, k_cache, v_cache,
+                              out, B, Hq, Hkv, D, max_length, position_id,
+                              seq_lens, scale, split_rows, workspace,
+                              workspace_bytes, 1, a);
+  if (st != ATTN_OK || a.B == 0) return st;
   hipError_t e = attn::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
@@ -258,6 +279,56 @@ int attn_decode_append(int dtype, const void *q, const void *k_new,
                      stream);
 }
 
+
+int attn_decode_paged(int dtype, const void *q, const void *k_pages,
+                      const void *v_pages, const int32_t *block_table,
+                      int max_blocks, int page_size, int num_pages,
+                      int page_layout, void *out,
+                      int B, int Hq, int Hkv, int D, int position_id,
+                      const int32_t *seq_lens, float scale, int split_rows,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  const char *fn = "attn_decode_paged";
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_E_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (dtype != ATTN_BF16)
+    return fail(ATTN_E_UNSUPPORTED, "%s: only ATTN_BF16 is supported", fn);
+  if (D != 64 && D != 128)
+    return fail(D < 1 ? ATTN_E_ARG : ATTN_E_UNSUPPORTED, "%s: D=%d not in {64,128}", fn, D);
+  const int tile = 4096 / D;  // rows of one wave tile
+  if (page_size < 1 || max_blocks < 1 || num_pages < 1)
+    return fail(ATTN_E_ARG, "%s: page_size=%d max_blocks=%d num_pages=%d must be >= 1",
+                fn, page_size, max_blocks, num_pages);
+  if (page_layout != ATTN_PAGES_TOKEN_MAJOR && page_layout != ATTN_PAGES_HEAD_MAJOR)
+    return fail(ATTN_E_ARG, "%s: unknown page_layout %d", fn, page_layout);
+  if (page_size % tile != 0 || page_size > 65536)
+    return fail(ATTN_E_UNSUPPORTED, "%s: page_size=%d is not a multiple of %d in [%d, 65536]",
+                fn, page_size, tile, tile);
+  if ((long long)max_blocks * page_size > 0x7fffffffLL ||
+      !fits({(double)num_pages, (double)page_size, (double)Hkv, (double)D, 2.0}))
+    return fail(ATTN_E_ARG, "%s: page extents overflow", fn);
+  const int max_length = max_blocks * page_size;
+  if (B > 0 && !block_table)
+    return fail(ATTN_E_ARG, "%s: null block_table", fn);
+  if (block_table && !aligned(block_table, 4))
+    return fail(ATTN_E_ARG, "%s: block_table must be 4-byte aligned", fn);
+  // The remaining checks are those of the logical cache
+  // [B][Hkv][max_length][D]; split lengths become multiples of the wave tile
+  // so that no tile straddles a page.
+  attn::DecodeArgs a;
+  const int st = decode_check(fn, dtype, q, nullptr, nullptr, k_pages, v_pages,
+                              out, B, Hq, Hkv, D, max_length, position_id,
+                              seq_lens, scale, split_rows, workspace,
+                              workspace_bytes, tile, a);
+  if (st != ATTN_OK || a.B == 0) return st;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  a.head_major = page_layout == ATTN_PAGES_HEAD_MAJOR;
+  hipError_t e = attn::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
 
 int attn_prefill(int dtype, const void *q, const void *k_cache,
                  const void *v_cache, void *out, int B, int Hq, int Hkv, int D,

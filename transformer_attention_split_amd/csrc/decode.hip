@@ -212,7 +212,9 @@ struct Bf16Tile {
   static_assert(NOCT * (D / 8) == 64, "one V transpose item per lane");
 };
 
-template <int D, int G, bool APPEND>
+// MODE: 0 = contiguous cache, 1 = contiguous cache with the fused append,
+// 2 = paged cache.
+template <int D, int G, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     const uint16_t *__restrict__ qg, const uint16_t *__restrict__ kg,
     const uint16_t *__restrict__ vg, const int32_t *__restrict__ seq_lens,
@@ -220,7 +222,10 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     float *__restrict__ ws_o, int Hq, int Hkv,
     int max_length, int split_rows, int splits, float qk_scale,
     const uint16_t *__restrict__ knew, const uint16_t *__restrict__ vnew,
-    uint16_t *kw, uint16_t *vw) {
+    uint16_t *kw, uint16_t *vw, const int32_t *__restrict__ block_table,
+    int max_blocks, int page_size, int num_pages, int head_major) {
+  constexpr bool APPEND = MODE == 1;
+  constexpr bool PAGED = MODE == 2;
   using T = Bf16Tile<D>;
   constexpr int BN = T::BN, KS = T::KS, NDB = T::NDB, NKB = T::NKB;
   constexpr int SV = T::SV;
@@ -239,7 +244,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     return;
   }
   const int tid = threadIdx.x;
-  const int w = tid / 64;
+  // (uniform wave index in a scalar register where the paged tile lookup
+  // depends on it)
+  const int w = PAGED ? __builtin_amdgcn_readfirstlane(tid / 64) : tid / 64;
   const int l = tid % 64;
   const int li = l % 16;   // query column / row within a 16-row block
   const int lg = l / 16;   // lane group (k slots 8*lg..8*lg+7)
@@ -259,6 +266,27 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   const size_t kvbase = ((size_t)b * Hkv + g) * (size_t)max_length * D;
   const uint16_t *kb = kg + kvbase;
   const uint16_t *vb = vg + kvbase;
+  // Paged caches: row r of sequence b is row r % page_size of page
+  // block_table[b][r / page_size] (clamped to the pages that exist), pages
+  // token-major [page][row][Hkv][D] (consecutive rows of one kv head Hkv*D
+  // elements apart) or head-major [page][Hkv][row][D] (rows of a head
+  // contiguous). A tile (BN rows from a multiple of BN) never straddles a
+  // page.
+  const size_t prs = head_major ? (size_t)D : (size_t)Hkv * D;
+  // (the lookup is made on wave-uniform values so that it is a scalar load:
+  // a vector load would complete in order behind the K/V loads in flight)
+  const int bu = __builtin_amdgcn_readfirstlane(b);
+  const int gu = __builtin_amdgcn_readfirstlane(g);
+  auto page_of = [&](int t0) {
+    const int tu = __builtin_amdgcn_readfirstlane(t0);
+    const int pg = block_table[(size_t)bu * max_blocks + tu / page_size];
+    return min(max(pg, 0), num_pages - 1);
+  };
+  auto page_tile = [&](const uint16_t *base, int pg, int t0) {
+    const int tu = __builtin_amdgcn_readfirstlane(t0);
+    return base + (head_major ? (((size_t)pg * Hkv + gu) * page_size + tu % page_size) * D
+                              : ((size_t)pg * page_size + tu % page_size) * prs + (size_t)gu * D);
+  };
   // Appending: the sequence's last valid row is the new token. Its K and V
   // are read from knew / vnew (so no workgroup reads that cache row while it
   // is being written) and split 0 stores them into the cache.
@@ -290,23 +318,28 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   // (a partial last tile reads valid rows; they are masked).
   const int last_row = it.row1 - 1;
   u32x4_t kf[NKB][KS], vr[8];
-  auto load_k = [&](int t0) {
+  auto load_k = [&](int t0, int pg) {
+    const uint16_t *kt = PAGED ? page_tile(kg, pg, t0) : nullptr;
 #pragma unroll
     for (int kb16 = 0; kb16 < NKB; ++kb16) {
       const int row = min(t0 + kb16 * 16 + li, last_row);
+      const uint16_t *src = PAGED ? kt + (size_t)(row - t0) * prs
+                                  : (APPEND && row == arow ? kn : kb + (size_t)row * D);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[kb16][ks] = ldnt((APPEND && row == arow ? kn : kb + (size_t)row * D) + ks * 32 + 8 * lg);
+      for (int ks = 0; ks < KS; ++ks) kf[kb16][ks] = ldnt(src + ks * 32 + 8 * lg);
     }
   };
-  auto load_v = [&](int t0) {
+  auto load_v = [&](int t0, int pg) {
+    const uint16_t *vtl = PAGED ? page_tile(vg, pg, t0) : nullptr;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = min(t0 + 8 * oct + i, last_row);
-      vr[i] = ldnt((APPEND && row == arow ? vn : vb + (size_t)row * D) + 8 * ch);
+      const uint16_t *src = PAGED ? vtl + (size_t)(row - t0) * prs
+                                  : (APPEND && row == arow ? vn : vb + (size_t)row * D);
+      vr[i] = ldnt(src + 8 * ch);
     }
   };
-  auto compute_tile = [&](int t0, int tnext) {
+  auto compute_tile = [&](int t0, int tnext, int pgnext) {
     const bool full = t0 + BN <= it.row1;
     // ---- Sᵀ = K·Qᵀ --------------------------------------------------------------
     f32x4_t sc[NKB];
@@ -318,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
         sc[kb16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(kf[kb16][ks]), qf[ks], sc[kb16], 0, 0, 0);
     }
-    if (tnext >= 0) load_k(tnext);
+    if (tnext >= 0) load_k(tnext, pgnext);
     // ---- V rows -> Vᵀ in LDS (keys 8*oct..8*oct+7 of dims 8*ch..8*ch+7) ----
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -335,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
       dst[0] = u32x2_t{pk[0], pk[1]};
       dst[1] = u32x2_t{pk[2], pk[3]};
     }
-    if (tnext >= 0) load_v(tnext);
+    if (tnext >= 0) load_v(tnext, pgnext);
     // ---- online softmax -----------------------------------------------------------
     float mx = kNegInf;
 #pragma unroll
@@ -391,11 +424,15 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   };
   for (int t0 = it.row0 + w * BN, first = 1; t0 < it.row1; t0 += 4 * BN, first = 0) {
     if (first) {
-      load_k(t0);
-      load_v(t0);
+      const int pg0 = PAGED ? page_of(t0) : 0;
+      load_k(t0, pg0);
+      load_v(t0, pg0);
     }
     const int t1 = t0 + 4 * BN;
-    compute_tile(t0, t1 < it.row1 ? t1 : -1);
+    // (the next tile's page is looked up before this tile's products, so the
+    // scalar load has completed when the next tile's loads are issued)
+    const int pg1 = PAGED && t1 < it.row1 ? page_of(t1) : 0;
+    compute_tile(t0, t1 < it.row1 ? t1 : -1, pg1);
   }
 
   // ---- merge the 4 waves -----------------------------------------------------------
@@ -706,19 +743,21 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   }
 }
 
-template <bool BF16, int D, int G, bool APPEND>
+template <bool BF16, int D, int G, int MODE>
 void launch_split(const DecodeArgs &a, hipStream_t stream) {
   dim3 grid(a.Hkv, a.B, a.plan.splits);
   if constexpr (BF16) {
-    decode_bf16_kernel<D, G, APPEND><<<grid, kThreads, 0, stream>>>(
+    decode_bf16_kernel<D, G, MODE><<<grid, kThreads, 0, stream>>>(
         static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
         static_cast<const uint16_t *>(a.v), a.seq_lens, a.position_id, a.out,
         a.ws_ml, a.ws_o, a.Hq, a.Hkv, a.max_length,
         a.plan.split_rows, a.plan.splits, a.scale * kLog2e,
         static_cast<const uint16_t *>(a.k_new), static_cast<const uint16_t *>(a.v_new),
-        static_cast<uint16_t *>(a.k_w), static_cast<uint16_t *>(a.v_w));
+        static_cast<uint16_t *>(a.k_w), static_cast<uint16_t *>(a.v_w),
+        a.block_table, a.max_blocks, a.page_size, a.num_pages, a.head_major);
   } else {
-    decode_f32_kernel<D, G, APPEND><<<grid, kThreads, 0, stream>>>(
+    static_assert(MODE != 2, "paged caches are bf16 only");
+    decode_f32_kernel<D, G, MODE == 1><<<grid, kThreads, 0, stream>>>(
         static_cast<const float *>(a.q), static_cast<const float *>(a.k),
         static_cast<const float *>(a.v), a.seq_lens, a.position_id, a.out,
         a.ws_ml, a.ws_o, a.Hq, a.Hkv, a.max_length,
@@ -731,9 +770,15 @@ void launch_split(const DecodeArgs &a, hipStream_t stream) {
 template <bool BF16, int D, int G>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
   if (a.k_new != nullptr)
-    launch_split<BF16, D, G, true>(a, stream);
-  else
-    launch_split<BF16, D, G, false>(a, stream);
+    launch_split<BF16, D, G, 1>(a, stream);
+  else if constexpr (BF16) {
+    if (a.block_table != nullptr)
+      launch_split<BF16, D, G, 2>(a, stream);
+    else
+      launch_split<BF16, D, G, 0>(a, stream);
+  } else {
+    launch_split<BF16, D, G, 0>(a, stream);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.plan.splits <= 1) return e;
   decode_combine_kernel<BF16, D><<<dim3(a.Hq, a.B), 64, 0, stream>>>(

@@ -35,6 +35,13 @@ struct DecodeArgs {
   // (the same memory as k / v) and attended to in the same launch.
   const void *k_new = nullptr, *v_new = nullptr;
   void *k_w = nullptr, *v_w = nullptr;
+  // Paged caches (bf16 only; null for a contiguous cache): k / v are
+  // [num_pages][page_size][Hkv][D] (or head-major, below); block_table [B][max_blocks] gives the page
+  // of every page_size rows of each sequence; max_length = max_blocks *
+  // page_size and split_rows is a multiple of the wave tile.
+  const int32_t *block_table = nullptr;
+  int max_blocks = 0, page_size = 0, num_pages = 0;
+  int head_major = 0;  // pages [num_pages][Hkv][page_size][D] instead
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
