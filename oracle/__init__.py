@@ -11,6 +11,8 @@ from .attention import (  # noqa: F401
     decode_paged,
     decode_sequence,
     prefill,
+    topk_causal_select,
+    topk_causal_sparse,
     topk_sparse,
     topk_scores,
     topk_select,

@@ -269,3 +269,60 @@ def topk_sparse(q: np.ndarray, k: np.ndarray, v: np.ndarray, topk: int,
     if return_details:
         return out, idx_all, gap_all
     return out
+
+
+def topk_causal_select(s_row: np.ndarray, i: int, topk: int) -> np.ndarray:
+    """Key indices row i keeps in the decoder form of top-k sparsification
+    [P3 "further thoughts": a causal model attends only to the tokens on its
+    left, and each query keeps its most recent k/2 tokens]. Reading:
+
+    * the candidates are j <= i (the query's own token included);
+    * when i + 1 <= topk every candidate is kept (nothing to sparsify);
+    * otherwise the r = floor(topk / 2) most recent keys, j in (i - r, i],
+      are kept unconditionally and the remaining topk - r slots go to the
+      largest scores among the older keys j <= i - r, equal scores to the
+      lower index (as in ``topk_select``).
+
+    Returns the kept indices in ascending order (min(topk, i + 1) of them).
+    """
+    if i + 1 <= topk:
+        return np.arange(i + 1)
+    r = topk // 2
+    older = s_row[: i + 1 - r]
+    best = np.argsort(-older, kind="stable")[: topk - r]
+    return np.sort(np.concatenate([best, np.arange(i + 1 - r, i + 1)]))
+
+
+def topk_causal_sparse(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                       topk: int, return_details: bool = False):
+    """Decoder-causal top-k sparse attention: the scores of [P3 §2] (q·kᵀ,
+    no scale, no softmax), with row i keeping the keys chosen by
+    ``topk_causal_select``; every other entry of row i is zero, and the
+    output row is the kept scores times the kept rows of v.
+
+    q, k, v: [b, h, n, d] float32. Returns float64 [b, h, n, d]; with
+    ``return_details`` also the kept indices [b, h, n, topk] (ascending,
+    padded with -1 when a row keeps fewer than topk) and, per row, the gap
+    between the last older score taken and the first one left out (+inf
+    when the row keeps every candidate or no older key is left out).
+    """
+    bsz, H, n, d = q.shape
+    out = np.zeros((bsz, H, n, d), dtype=np.float64)
+    idx_all = np.full((bsz, H, n, topk), -1, dtype=np.int64)
+    gap_all = np.full((bsz, H, n), np.inf, dtype=np.float64)
+    r = topk // 2
+    for b in range(bsz):
+        for h in range(H):
+            s = topk_scores(q[b, h], k[b, h])                    # [n, n]
+            v64 = np.asarray(v[b, h], dtype=np.float64)
+            for i in range(n):
+                sel = topk_causal_select(s[i], i, topk)
+                out[b, h, i] = s[i, sel] @ v64[sel]
+                idx_all[b, h, i, : len(sel)] = sel
+                n_old = i + 1 - r
+                if i + 1 > topk and topk - r < n_old:
+                    srt = -np.sort(-s[i, :n_old])
+                    gap_all[b, h, i] = srt[topk - r - 1] - srt[topk - r]
+    if return_details:
+        return out, idx_all, gap_all
+    return out

@@ -490,6 +490,132 @@ def test_topk_zero_query_selects_first_indices():
     assert np.all(out == 0)
 
 
+# ----------------------------------------------------------------------------
+# Decoder-causal top-k (c2psa page, further thoughts)
+# ----------------------------------------------------------------------------
+def test_topk_causal_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "topk_causal_hand.json")))
+    q = np.array(g["q"], np.float32)
+    k = np.array(g["k"], np.float32)
+    v = np.array(g["v"], np.float32)
+    for case in g["cases"]:
+        out, idx, _ = oracle.topk_causal_sparse(q, k, v, case["topk"],
+                                                return_details=True)
+        np.testing.assert_allclose(out[0, 0], np.array(case["expected"]),
+                                   rtol=0, atol=g["tolerance"])
+        assert idx[0, 0].tolist() == case["indices"]
+
+
+def test_topk_causal_brute_force_over_admissible_subsets():
+    # Row i keeps c = min(topk, i+1) keys among j <= i; when i+1 > topk the
+    # r = topk//2 most recent are forced. Among every admissible c-subset,
+    # the kept one has the largest older scores, ties to the lower index
+    # (lexicographically smallest sorted (-score, index) tuple of its older
+    # part). Enumerate all of them on integer data full of ties.
+    rng = np.random.default_rng(41)
+    n, d = 8, 3
+    for trial in range(4):
+        q = rng.integers(-2, 3, (1, 1, n, d)).astype(np.float32)
+        k = rng.integers(-2, 3, (1, 1, n, d)).astype(np.float32)
+        v = rng.standard_normal((1, 1, n, d)).astype(np.float32)
+        for topk in (1, 2, 3, 4, 5, 8):
+            out, idx, _ = oracle.topk_causal_sparse(q, k, v, topk,
+                                                    return_details=True)
+            r = topk // 2
+            for i in range(n):
+                s = [float(np.dot(q[0, 0, i].astype(np.float64),
+                                  k[0, 0, j].astype(np.float64)))
+                     for j in range(n)]
+                c = min(topk, i + 1)
+                forced = set(range(i + 1 - r, i + 1)) if i + 1 > topk else set()
+                best = None
+                for sub in itertools.combinations(range(i + 1), c):
+                    if not forced <= set(sub):
+                        continue
+                    key = tuple(sorted((-s[j], j) for j in sub
+                                       if j not in forced))
+                    if best is None or key < best[0]:
+                        best = (key, sub)
+                assert tuple(idx[0, 0, i, :c]) == best[1]
+                assert np.all(idx[0, 0, i, c:] == -1)
+                expect = sum(s[j] * v[0, 0, j].astype(np.float64)
+                             for j in best[1])
+                np.testing.assert_allclose(out[0, 0, i], expect, rtol=0,
+                                           atol=1e-12)
+
+
+def test_topk_causal_k_at_least_n_is_lower_triangular_product():
+    rng = np.random.default_rng(42)
+    q = rng.standard_normal((2, 3, 20, 8)).astype(np.float32)
+    k = rng.standard_normal((2, 3, 20, 8)).astype(np.float32)
+    v = rng.standard_normal((2, 3, 20, 8)).astype(np.float32)
+    out = oracle.topk_causal_sparse(q, k, v, 20)
+    s = torch.matmul(_t(q), _t(k).transpose(-2, -1))
+    ref = torch.matmul(torch.tril(s), _t(v)).numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-11)
+
+
+def test_topk_causal_k1_is_causal_max_times_its_row():
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((1, 2, 16, 8)).astype(np.float32)
+    k = rng.standard_normal((1, 2, 16, 8)).astype(np.float32)
+    v = rng.standard_normal((1, 2, 16, 8)).astype(np.float32)
+    out = oracle.topk_causal_sparse(q, k, v, 1)
+    s = torch.matmul(_t(q), _t(k).transpose(-2, -1))
+    s = s.masked_fill(torch.ones(16, 16, dtype=torch.bool).triu(1),
+                      float("-inf"))
+    smax, arg = s.max(dim=-1)
+    ref = smax[..., None] * torch.gather(
+        _t(v), 2, arg[..., None].expand(-1, -1, -1, 8))
+    np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("topk", [2, 7, 10, 16])
+def test_topk_causal_matches_masked_topk_scatter_plus_recent_band(topk):
+    # The page's torch.topk + scatter form applied to the older keys only
+    # (later keys masked to -inf), plus the band of the r most recent
+    # scores; rows with i+1 <= topk take the plain lower triangle. Data
+    # without ties.
+    rng = np.random.default_rng(44)
+    n = 40
+    q = rng.standard_normal((2, 2, n, 16)).astype(np.float32)
+    k = rng.standard_normal((2, 2, n, 16)).astype(np.float32)
+    v = rng.standard_normal((2, 2, n, 16)).astype(np.float32)
+    r = topk // 2
+    s = torch.matmul(_t(q), _t(k).transpose(-2, -1))
+    ii = torch.arange(n)[:, None]
+    jj = torch.arange(n)[None, :]
+    older = s.masked_fill(jj > ii - r, float("-inf"))
+    val, idx = torch.topk(older, k=topk - r, dim=-1)
+    sparse = torch.zeros_like(s).scatter(-1, idx, val)
+    sparse = torch.where((jj <= ii) & (jj > ii - r), s, sparse)
+    sparse = torch.where(ii + 1 <= topk, torch.tril(s), sparse)
+    ref = torch.matmul(sparse, _t(v)).numpy()
+    out, myidx, gap = oracle.topk_causal_sparse(q, k, v, topk,
+                                                return_details=True)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-11)
+    assert np.all(np.isinf(gap[..., :topk])) and np.all(gap[..., topk:] > 0)
+
+
+def test_topk_causal_rows_respect_order_and_recency():
+    rng = np.random.default_rng(45)
+    n, topk = 50, 12
+    q = rng.standard_normal((1, 1, n, 8)).astype(np.float32)
+    k = rng.standard_normal((1, 1, n, 8)).astype(np.float32)
+    v = rng.standard_normal((1, 1, n, 8)).astype(np.float32)
+    _, idx, _ = oracle.topk_causal_sparse(q, k, v, topk, return_details=True)
+    s = oracle.topk_scores(q[0, 0], k[0, 0])
+    for i in range(n):
+        row = [j for j in idx[0, 0, i].tolist() if j >= 0]
+        assert len(row) == min(topk, i + 1) and row == sorted(set(row))
+        assert max(row) <= i                      # no key to the right
+        if i + 1 > topk:
+            assert set(range(i - topk // 2 + 1, i + 1)) <= set(row)
+            old_in = [j for j in row if j <= i - topk // 2]
+            old_out = [j for j in range(i - topk // 2 + 1) if j not in row]
+            assert min(s[i, old_in]) >= max(s[i, old_out])
+
+
 @pytest.mark.slow
 def test_fp32_accumulation_is_not_enough_for_topk_tolerance():
     # Why the kernel accumulates top-k scores and outputs in fp64: on the
