@@ -100,12 +100,17 @@ def make_prefill(torch, synth):
 
 
 def make_topk(torch, synth):
+    import numpy as np
     p = synth.WORKLOADS["topk_c2psa"].params
     inp = synth.topk(p["seed"], p["b"], p["h"], p["n"], p["d"], p["topk"])
     q, k, v = (torch.from_numpy(x).cuda() for x in (inp.q, inp.k, inp.v))
     b, h, n, d, kk = p["b"], p["h"], p["n"], p["d"], p["topk"]
     flops = b * h * (2 * n * n * d + 2 * n * kk * d)
-    return dict(p=p, q=q, k=k, v=v, out=torch.empty_like(q), flops=flops)
+    # decoder-causal form: row i scores keys j <= i and sums min(k, i+1) rows
+    rows = np.arange(1, n + 1)
+    flops_causal = int(b * h * 2 * d * (rows.sum() + np.minimum(kk, rows).sum()))
+    return dict(p=p, q=q, k=k, v=v, out=torch.empty_like(q), flops=flops,
+                flops_causal=flops_causal)
 
 
 # ----------------------------------------------------------------------------
@@ -445,6 +450,8 @@ def main():
         scale=pp["scale"], out=pre["out"]))
     t_tk_b2b = back_to_back(lambda: tas.attn_topk(
         tk["q"], tk["k"], tk["v"], tk["p"]["topk"], out=tk["out"]))
+    t_tkc_b2b = back_to_back(lambda: tas.attn_topk_causal(
+        tk["q"], tk["k"], tk["v"], tk["p"]["topk"], out=tk["out"]))
 
     def pct(i):
         xs = np.array([e[i].elapsed_time(e[i + 1]) * 1e3 for e in evs])
@@ -473,6 +480,11 @@ def main():
                      frac_of_fp64_peak=round(tk_tflops / FP64_PEAK_TFLOPS, 4),
                      flops=tk["flops"], us_percentiles=tk_pct,
                      us_back_to_back=round(t_tk_b2b, 2)),
+        "topk_causal": dict(workload="topk_c2psa, decoder-causal form",
+                            us_back_to_back=round(t_tkc_b2b, 2),
+                            flops=tk["flops_causal"],
+                            TFLOPs_back_to_back=round(
+                                tk["flops_causal"] / t_tkc_b2b / 1e6, 3)),
     }
     if not args.no_secondary:
         log("fused append + decode on the ragged batch ...")

@@ -24,6 +24,10 @@
  *                 Source: "c2psa multi-head self-attention high-concurrency
  *                 inference", core implementation §2 (dynamic top-k
  *                 sparsification) and the full C2PSA class (topk=64).
+ *   attn_topk_causal  the same scores in the decoder form: a query chooses
+ *                 only among keys on its left and always keeps its most
+ *                 recent topk/2.
+ *                 Source: the same page, further thoughts.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -242,6 +246,26 @@ int attn_prefill(int dtype, const void *q, const void *k_cache,
 int attn_topk(const float *q, const float *k, const float *v, float *out,
               int32_t *idx_out, int b, int h, int n, int d, int topk,
               void *stream);
+
+/* Decoder-causal top-k sparsified scores.
+ * Source: "c2psa multi-head self-attention high-concurrency inference",
+ * further thoughts (in a decoder a query attends only to the tokens on its
+ * left and keeps its most recent k/2 tokens), applied to the scores of core
+ * implementation §2. The pages give no more of the rule; this library reads
+ * it as: for every (b, h) and query row i, the candidates are the keys
+ * j <= i (its own token included), s_ij = Σ_d q[i,d]·k[j,d] with no scale;
+ *   - if i+1 <= topk, S_i = {0, ..., i} (every candidate);
+ *   - else, with r = floor(topk/2), S_i = {i-r+1, ..., i} (kept whatever
+ *     their scores) plus the topk-r keys j <= i-r with the largest s_ij
+ *     (equal scores: the lower index first);
+ * out[i,:] = Σ_{j∈S_i} s_ij · v[j,:]; no softmax.
+ *
+ * Arguments, layouts, precision, limits and errors are those of attn_topk.
+ * idx_out (optional) [b][h][n][topk] receives S_i in ascending order,
+ * followed by -1 in the topk - |S_i| slots of rows with i+1 < topk. */
+int attn_topk_causal(const float *q, const float *k, const float *v, float *out,
+                     int32_t *idx_out, int b, int h, int n, int d, int topk,
+                     void *stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

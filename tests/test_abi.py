@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_three_operations():
     names = declared_functions()
     for n in ("attn_decode", "attn_prefill", "attn_topk",
-              "attn_decode_workspace_bytes", "attn_status_str"):
+              "attn_topk_causal", "attn_decode_workspace_bytes",
+              "attn_status_str"):
         assert n in names
 
 
@@ -240,12 +241,13 @@ def test_prefill_empty_is_a_noop():
 # ----------------------------------------------------------------------------
 # topk
 # ----------------------------------------------------------------------------
-def topk(**kw):
+def topk(fn="attn_topk", **kw):
     a = dict(q=P, k=P, v=P, out=P, idx=None, b=32, h=3, n=512, d=64, topk=64,
              stream=None)
     a.update(kw)
-    return lib.attn_topk(a["q"], a["k"], a["v"], a["out"], a["idx"], a["b"],
-                         a["h"], a["n"], a["d"], a["topk"], a["stream"])
+    return getattr(lib, fn)(a["q"], a["k"], a["v"], a["out"], a["idx"],
+                            a["b"], a["h"], a["n"], a["d"], a["topk"],
+                            a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -262,13 +264,16 @@ def topk(**kw):
     (dict(k=P + 4), E_ARG),
     (dict(idx=P + 2), E_ARG),
 ])
-def test_topk_rejects(kw, status):
-    assert topk(**kw) == status
+@pytest.mark.parametrize("fn", ["attn_topk", "attn_topk_causal"])
+def test_topk_rejects(fn, kw, status):
+    assert topk(fn, **kw) == status
+    assert fn in lib.attn_last_error().decode()
 
 
-def test_topk_empty_is_a_noop():
-    assert topk(b=0) == OK
-    assert topk(h=0) == OK
+@pytest.mark.parametrize("fn", ["attn_topk", "attn_topk_causal"])
+def test_topk_empty_is_a_noop(fn):
+    assert topk(fn, b=0) == OK
+    assert topk(fn, h=0) == OK
 
 
 def test_python_binding_raises_with_reason():

@@ -20,9 +20,10 @@ from ._binding import (  # noqa: F401
     attn_decode_workspace_bytes,
     attn_prefill,
     attn_topk,
+    attn_topk_causal,
     lib,
 )
 
 __all__ = ["attn_decode", "attn_decode_append", "attn_decode_paged",
-           "attn_prefill", "attn_topk",
+           "attn_prefill", "attn_topk", "attn_topk_causal",
            "attn_decode_workspace_bytes", "AttnError", "AttnArgError"]

@@ -25,7 +25,7 @@ ATTN_PAGES_TOKEN_MAJOR, ATTN_PAGES_HEAD_MAJOR = 0, 1
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build it with "
-        "`python -m transformer_attention_split_amd.build`")
+        "`python transformer_attention_split_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -56,10 +56,13 @@ lib.attn_prefill.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
                              _f, _p]
 lib.attn_topk.restype = _i
 lib.attn_topk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+lib.attn_topk_causal.restype = _i
+lib.attn_topk_causal.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 
 EXPORTED = ("attn_status_str", "attn_last_error", "attn_abi_version",
             "attn_decode_workspace_bytes", "attn_decode", "attn_decode_append",
-            "attn_decode_paged", "attn_prefill", "attn_topk")
+            "attn_decode_paged", "attn_prefill", "attn_topk",
+            "attn_topk_causal")
 
 
 class AttnError(RuntimeError):
@@ -313,13 +316,9 @@ def attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 # ----------------------------------------------------------------------------
 # Top-k
 # ----------------------------------------------------------------------------
-def attn_topk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
-              *, out: Optional[torch.Tensor] = None,
-              idx_out: Optional[torch.Tensor] = None,
-              stream=None) -> torch.Tensor:
-    """Top-k sparse attention. q, k, v float32 [b,h,n,d]. Returns out
-    [b,h,n,d]; if ``idx_out`` (int32 [b,h,n,topk]) is given it receives the
-    selected indices of each row in ascending order."""
+def _topk_call(fn: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+               topk: int, out: Optional[torch.Tensor],
+               idx_out: Optional[torch.Tensor], stream) -> torch.Tensor:
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need_dense(name, t, 4)
         if t.dtype != torch.float32:
@@ -338,7 +337,28 @@ def attn_topk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
         if idx_out.dtype != torch.int32 or \
                 tuple(idx_out.shape) != (b, h, n, topk):
             raise ValueError("idx_out must be int32 [b,h,n,topk]")
-    st = lib.attn_topk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx_out),
-                       b, h, n, d, int(topk), _stream_handle(stream))
-    _check(st, "attn_topk")
+    st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx_out),
+                          b, h, n, d, int(topk), _stream_handle(stream))
+    _check(st, fn)
     return out
+
+
+def attn_topk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, topk: int,
+              *, out: Optional[torch.Tensor] = None,
+              idx_out: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """Top-k sparse attention. q, k, v float32 [b,h,n,d]. Returns out
+    [b,h,n,d]; if ``idx_out`` (int32 [b,h,n,topk]) is given it receives the
+    selected indices of each row in ascending order."""
+    return _topk_call("attn_topk", q, k, v, topk, out, idx_out, stream)
+
+
+def attn_topk_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     topk: int, *, out: Optional[torch.Tensor] = None,
+                     idx_out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Decoder-causal top-k sparse attention: row i chooses among keys
+    j <= i, keeping every one when i+1 <= topk, else its topk//2 most recent
+    plus the best-scoring older ones. Arguments as ``attn_topk``; rows that
+    keep fewer than ``topk`` keys pad ``idx_out`` with -1."""
+    return _topk_call("attn_topk_causal", q, k, v, topk, out, idx_out, stream)

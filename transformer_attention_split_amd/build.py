@@ -2,7 +2,8 @@
 
 Every source is compiled on each call (objects go to ``_build/`` at the
 repository root) and linked into ``transformer_attention_split_amd/libattn.so``.
-Run as ``python -m transformer_attention_split_amd.build``.
+Run as ``python transformer_attention_split_amd/build.py`` (by path, so that
+the package, which loads the library on import, is not imported first).
 """
 from __future__ import annotations
 

@@ -371,33 +371,46 @@ int attn_prefill(int dtype, const void *q, const void *k_cache,
   return ok();
 }
 
-int attn_topk(const float *q, const float *k, const float *v, float *out,
-              int32_t *idx_out, int b, int h, int n, int d, int topk,
-              void *stream) {
+static int topk_impl(const char *fn, bool causal, const float *q, const float *k,
+                     const float *v, float *out, int32_t *idx_out, int b, int h,
+                     int n, int d, int topk, void *stream) {
   if (b < 0 || b > 65535 || h < 0 || h > 65535)
-    return fail(ATTN_E_ARG, "attn_topk: b=%d h=%d outside [0, 65535]", b, h);
-  if (d < 1) return fail(ATTN_E_ARG, "attn_topk: d=%d", d);
-  if (d != 64) return fail(ATTN_E_UNSUPPORTED, "attn_topk: d=%d, only 64", d);
-  if (n < 1) return fail(ATTN_E_ARG, "attn_topk: n=%d must be >= 1", n);
-  if (n > 1024) return fail(ATTN_E_UNSUPPORTED, "attn_topk: n=%d > 1024", n);
+    return fail(ATTN_E_ARG, "%s: b=%d h=%d outside [0, 65535]", fn, b, h);
+  if (d < 1) return fail(ATTN_E_ARG, "%s: d=%d", fn, d);
+  if (d != 64) return fail(ATTN_E_UNSUPPORTED, "%s: d=%d, only 64", fn, d);
+  if (n < 1) return fail(ATTN_E_ARG, "%s: n=%d must be >= 1", fn, n);
+  if (n > 1024) return fail(ATTN_E_UNSUPPORTED, "%s: n=%d > 1024", fn, n);
   if (topk < 1 || topk > n)
-    return fail(ATTN_E_ARG, "attn_topk: topk=%d outside [1, n=%d]", topk, n);
+    return fail(ATTN_E_ARG, "%s: topk=%d outside [1, n=%d]", fn, topk, n);
   if ((int64_t)b * h * ((n + 15) / 16) > (int64_t)1 << 23)
     return fail(ATTN_E_UNSUPPORTED,
-                "attn_topk: b*h*ceil(n/16)=%lld workgroups > 2^23",
+                "%s: b*h*ceil(n/16)=%lld workgroups > 2^23", fn,
                 (long long)b * h * ((n + 15) / 16));
   if (b == 0 || h == 0) return ok();  // nothing is read or written
   if (!q || !k || !v || !out)
-    return fail(ATTN_E_ARG, "attn_topk: null data pointer");
+    return fail(ATTN_E_ARG, "%s: null data pointer", fn);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
       !aligned(out, 16))
-    return fail(ATTN_E_ARG, "attn_topk: data pointers must be 16-byte aligned");
+    return fail(ATTN_E_ARG, "%s: data pointers must be 16-byte aligned", fn);
   if (idx_out && !aligned(idx_out, 4))
-    return fail(ATTN_E_ARG, "attn_topk: idx_out must be 4-byte aligned");
-  attn::TopkArgs a{q, k, v, out, idx_out, b, h, n, d, topk};
+    return fail(ATTN_E_ARG, "%s: idx_out must be 4-byte aligned", fn);
+  attn::TopkArgs a{q, k, v, out, idx_out, b, h, n, d, topk, causal};
   hipError_t e = attn::launch_topk(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "attn_topk launch");
+  if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
+}
+
+int attn_topk(const float *q, const float *k, const float *v, float *out,
+              int32_t *idx_out, int b, int h, int n, int d, int topk,
+              void *stream) {
+  return topk_impl("attn_topk", false, q, k, v, out, idx_out, b, h, n, d, topk, stream);
+}
+
+int attn_topk_causal(const float *q, const float *k, const float *v, float *out,
+                     int32_t *idx_out, int b, int h, int n, int d, int topk,
+                     void *stream) {
+  return topk_impl("attn_topk_causal", true, q, k, v, out, idx_out, b, h, n, d, topk,
+                   stream);
 }
 
 }  // extern "C"

@@ -60,6 +60,7 @@ struct TopkArgs {
   float *out;
   int32_t *idx;
   int b, h, n, d, topk;
+  bool causal = false;  // decoder form: keys j <= i, topk/2 most recent kept
 };
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);

@@ -5,6 +5,12 @@
 // of every row, zero the others, multiply the sparse matrix by v; no softmax.
 // Equal scores at the boundary go to the lower key index.
 //
+// Decoder form (same page, further thoughts): row i chooses only among keys
+// j <= i. A row with i+1 <= topk keeps all of them; a longer row keeps its
+// topk/2 most recent keys and chooses the other topk - topk/2 by score among
+// the older ones j <= i - topk/2. The score blocks past a workgroup's last
+// row are not computed.
+//
 // Precision: every fp32·fp32 product is exact in fp64, so scores and the
 // output sum are accumulated in fp64 and the selection is made on the fp64
 // scores; the output is rounded once to fp32.
@@ -96,7 +102,7 @@ __device__ __forceinline__ uint64_t order64(double x) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-template <int NTP>
+template <int NTP, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void topk_kernel(
     const float *__restrict__ qg, const float *__restrict__ kg,
     const float *__restrict__ vg, float *__restrict__ outg,
@@ -146,7 +152,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
         qa[4 * c + 3] = x[c].w;
       }
     }
-    const int nkb = (n + 15) / 16;
+    // causal: the block's rows see no key past its last row
+    const int nkb = ((CAUSAL ? min(n, q0 + QB) : n) + 15) / 16;
     // Two accumulators halve the dependent MFMA chain (the 64-term sum is
     // split into two halves of 32).
     auto load_kblk = [&](int blk, float4 (&x)[4]) {
@@ -198,146 +205,164 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
     const int i = 4 * w + ii;  // row inside the block
     const int qr = q0 + i;
     const bool row_ok = qr < n;  // uniform over the wave
+    // Keys the row keeps. Causal: a row with qr + 1 <= topk keeps every
+    // j <= qr; a longer one keeps its topk/2 most recent keys and chooses
+    // the other topk - topk/2 by score among the older keys j < lim.
+    const int cnt = CAUSAL ? min(topk, qr + 1) : topk;
+    const bool dense = CAUSAL && qr + 1 <= topk;
+    const int lim = CAUSAL ? qr + 1 - topk / 2 : n;
+    const int kk = CAUSAL ? topk - topk / 2 : topk;  // chosen by score
     if (row_ok) {
       // ---- 2. select ---------------------------------------------------------------
       double s[NTP];
-      bool ok[NTP];
-      float mxf = -__builtin_inff(), mnf = __builtin_inff();
 #pragma unroll
-      for (int t = 0; t < NTP; ++t) {
-        // read for every slot (padding too: in bounds, maybe stale) and then
-        // selected, so that no load waits behind a branch
+      for (int t = 0; t < NTP; ++t)  // every slot (padding too: in bounds, maybe stale)
         s[t] = S[i * NP + l + 64 * t] + 0.0;  // +0.0 turns -0 into +0
-        ok[t] = l + 64 * t < n;
-        mxf = fmaxf(mxf, ok[t] ? (float)s[t] : -__builtin_inff());
-        mnf = fminf(mnf, ok[t] ? (float)s[t] : __builtin_inff());
-      }
-      // (fp32-rounded range: any constants give a monotone map below)
-      const double mx = wave_extreme<true>(mxf), mn = wave_extreme<false>(mnf);
-      // Bucket of a score: a non-decreasing map of about [mn, mx] onto
-      // 0..255 (correctly rounded fma, truncation and clamping are all
-      // monotone), so a higher bucket means a strictly larger score. Equal
-      // scores share a bucket; a row of (nearly) equal scores is all bucket 0.
-      const double span = mx - mn;
-      const double bs = span > 1e-290 ? 256.0 / span : 0.0;
-      const double b0 = -mn * bs;
-      int bk[NTP];
+      uint64_t selm[NTP];
+      if (dense) {
 #pragma unroll
-      for (int t = 0; t < NTP; ++t) {
-        const int bb = (int)fma(s[t], bs, b0);
-        bk[t] = ok[t] ? min(max(bb, 0), 255) : -1;
-      }
-      // 256-bin histogram, scanned from the top: bucket B holds the topk-th
-      // largest score, gt scores lie in higher buckets, nc in B.
-      uint32_t *hist = hst + w * 256;
-#pragma unroll
-      for (int t = 0; t < NTP; ++t)
-        if (bk[t] >= 0) atomicAdd(&hist[bk[t]], 1u);
-      wave_sync();
-      int B, gt, nc;
-      {
-        // lane l holds bins 255-4l (top) .. 252-4l
-        const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(&hist[252 - 4 * l]);
-        const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
-        const uint32_t incl = wave_inclusive_scan(local, l);
-        const uint64_t hit = __ballot(incl >= (uint32_t)topk);
-        const int L = __ffsll((unsigned long long)hit) - 1;
-        uint32_t c = __builtin_amdgcn_readlane(incl - local, L);
-        const uint32_t h3 = __builtin_amdgcn_readlane(hv[3], L);
-        const uint32_t h2 = __builtin_amdgcn_readlane(hv[2], L);
-        const uint32_t h1 = __builtin_amdgcn_readlane(hv[1], L);
-        const uint32_t h0 = __builtin_amdgcn_readlane(hv[0], L);
-        int hb;
-        if (c + h3 >= (uint32_t)topk) { B = 255 - 4 * L; hb = h3; }
-        else if ((c += h3) + h2 >= (uint32_t)topk) { B = 254 - 4 * L; hb = h2; }
-        else if ((c += h2) + h1 >= (uint32_t)topk) { B = 253 - 4 * L; hb = h1; }
-        else { c += h1; B = 252 - 4 * L; hb = h0; }
-        gt = (int)c;
-        nc = hb;
-        *reinterpret_cast<u32x4_t *>(&hist[252 - 4 * l]) = u32x4_t{0u, 0u, 0u, 0u};
-      }
-      uint64_t selm[NTP], cm[NTP];
-#pragma unroll
-      for (int t = 0; t < NTP; ++t) {
-        selm[t] = __ballot(bk[t] > B);
-        cm[t] = __ballot(bk[t] == B);
-      }
-      const int need = topk - gt;  // 1 <= need <= nc
-      if (nc == need) {
-#pragma unroll
-        for (int t = 0; t < NTP; ++t) selm[t] |= cm[t];
-      } else if (nc <= 64) {
-        // The boundary bucket's candidates go to a per-wave list; each is
-        // ranked by (score descending, index ascending) and the candidate of
-        // rank need-1 is the last one taken.
-        double *cs = cand_s + w * 64;
-        int *cj = cand_j + w * 64;
-        int before = 0;
-#pragma unroll
-        for (int t = 0; t < NTP; ++t) {
-          if ((cm[t] >> l) & 1ull) {
-            const int pos = before + __popcll(cm[t] & below);
-            cs[pos] = s[t];
-            cj[pos] = l + 64 * t;
-          }
-          before += __popcll(cm[t]);
-        }
-        wave_sync();
-        const double my_s = cs[l < nc ? l : 0];
-        const int my_j = cj[l < nc ? l : 0];
-        // candidate m is in lane m: broadcast it with lane reads
-        const int my_lo = (int)(uint32_t)__double_as_longlong(my_s);
-        const int my_hi = (int)(uint32_t)(__double_as_longlong(my_s) >> 32);
-        int rank = 0;
-        for (int m = 0; m < nc; ++m) {
-          const uint64_t ob = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(my_hi, m) << 32) |
-                              (uint32_t)__builtin_amdgcn_readlane(my_lo, m);
-          const double os = __longlong_as_double((long long)ob);
-          const int oj = __builtin_amdgcn_readlane(my_j, m);
-          rank += (os > my_s || (os == my_s && oj < my_j)) ? 1 : 0;
-        }
-        const uint64_t last = __ballot(l < nc && rank == need - 1);
-        const int Ll = __ffsll((unsigned long long)last) - 1;
-        const double ts = __shfl(my_s, Ll);
-        const int tj = __shfl(my_j, Ll);
-#pragma unroll
-        for (int t = 0; t < NTP; ++t)
-          selm[t] |= __ballot(((cm[t] >> l) & 1ull) &&
-                              (s[t] > ts || (s[t] == ts && l + 64 * t <= tj)));
-        wave_sync();
+        for (int t = 0; t < NTP; ++t) selm[t] = __ballot(l + 64 * t <= qr);
       } else {
-        // Many equal or nearly equal scores: exact fp64 order among the
-        // candidates by a bisection over their 64-bit order keys.
-        uint64_t k64[NTP];
+        bool ok[NTP];
+        float mxf = -__builtin_inff(), mnf = __builtin_inff();
+#pragma unroll
+        for (int t = 0; t < NTP; ++t) {
+          ok[t] = l + 64 * t < lim;
+          mxf = fmaxf(mxf, ok[t] ? (float)s[t] : -__builtin_inff());
+          mnf = fminf(mnf, ok[t] ? (float)s[t] : __builtin_inff());
+        }
+        // (fp32-rounded range: any constants give a monotone map below)
+        const double mx = wave_extreme<true>(mxf), mn = wave_extreme<false>(mnf);
+        // Bucket of a score: a non-decreasing map of about [mn, mx] onto
+        // 0..255 (correctly rounded fma, truncation and clamping are all
+        // monotone), so a higher bucket means a strictly larger score. Equal
+        // scores share a bucket; a row of (nearly) equal scores is all bucket 0.
+        const double span = mx - mn;
+        const double bs = span > 1e-290 ? 256.0 / span : 0.0;
+        const double b0 = -mn * bs;
+        int bk[NTP];
+#pragma unroll
+        for (int t = 0; t < NTP; ++t) {
+          const int bb = (int)fma(s[t], bs, b0);
+          bk[t] = ok[t] ? min(max(bb, 0), 255) : -1;
+        }
+        // 256-bin histogram, scanned from the top: bucket B holds the topk-th
+        // largest score, gt scores lie in higher buckets, nc in B.
+        uint32_t *hist = hst + w * 256;
 #pragma unroll
         for (int t = 0; t < NTP; ++t)
-          k64[t] = ((cm[t] >> l) & 1ull) ? order64(s[t]) : 0ull;
-        uint64_t T2 = 0;
-        for (int bit = 63; bit >= 0; --bit) {
-          const uint64_t cand = T2 | (1ull << bit);
-          int cnt = 0;
-#pragma unroll
-          for (int t = 0; t < NTP; ++t) cnt += __popcll(__ballot(k64[t] >= cand));
-          if (cnt >= need) T2 = cand;
+          if (bk[t] >= 0) atomicAdd(&hist[bk[t]], 1u);
+        wave_sync();
+        int B, gt, nc;
+        {
+          // lane l holds bins 255-4l (top) .. 252-4l
+          const u32x4_t hv = *reinterpret_cast<const u32x4_t *>(&hist[252 - 4 * l]);
+          const uint32_t local = hv[0] + hv[1] + hv[2] + hv[3];
+          const uint32_t incl = wave_inclusive_scan(local, l);
+          const uint64_t hit = __ballot(incl >= (uint32_t)kk);
+          const int L = __ffsll((unsigned long long)hit) - 1;
+          uint32_t c = __builtin_amdgcn_readlane(incl - local, L);
+          const uint32_t h3 = __builtin_amdgcn_readlane(hv[3], L);
+          const uint32_t h2 = __builtin_amdgcn_readlane(hv[2], L);
+          const uint32_t h1 = __builtin_amdgcn_readlane(hv[1], L);
+          const uint32_t h0 = __builtin_amdgcn_readlane(hv[0], L);
+          int hb;
+          if (c + h3 >= (uint32_t)kk) { B = 255 - 4 * L; hb = h3; }
+          else if ((c += h3) + h2 >= (uint32_t)kk) { B = 254 - 4 * L; hb = h2; }
+          else if ((c += h2) + h1 >= (uint32_t)kk) { B = 253 - 4 * L; hb = h1; }
+          else { c += h1; B = 252 - 4 * L; hb = h0; }
+          gt = (int)c;
+          nc = hb;
+          *reinterpret_cast<u32x4_t *>(&hist[252 - 4 * l]) = u32x4_t{0u, 0u, 0u, 0u};
         }
-        int need2 = need;
+        uint64_t cm[NTP];
 #pragma unroll
         for (int t = 0; t < NTP; ++t) {
-          const uint64_t m = __ballot(k64[t] > T2);
-          selm[t] |= m;
-          need2 -= __popcll(m);
+          selm[t] = __ballot(bk[t] > B);
+          cm[t] = __ballot(bk[t] == B);
         }
-        // ties at T2: ascending key index = slot-major, lane-minor
-        for (int t = 0; t < NTP; ++t) {
-          uint64_t tm = __ballot(k64[t] == T2);
-          while (need2 > 0 && tm) {
-            const uint64_t low = tm & (~tm + 1ull);
-            selm[t] |= low;
-            tm ^= low;
-            --need2;
+        const int need = kk - gt;  // 1 <= need <= nc
+        if (nc == need) {
+#pragma unroll
+          for (int t = 0; t < NTP; ++t) selm[t] |= cm[t];
+        } else if (nc <= 64) {
+          // The boundary bucket's candidates go to a per-wave list; each is
+          // ranked by (score descending, index ascending) and the candidate of
+          // rank need-1 is the last one taken.
+          double *cs = cand_s + w * 64;
+          int *cj = cand_j + w * 64;
+          int before = 0;
+#pragma unroll
+          for (int t = 0; t < NTP; ++t) {
+            if ((cm[t] >> l) & 1ull) {
+              const int pos = before + __popcll(cm[t] & below);
+              cs[pos] = s[t];
+              cj[pos] = l + 64 * t;
+            }
+            before += __popcll(cm[t]);
+          }
+          wave_sync();
+          const double my_s = cs[l < nc ? l : 0];
+          const int my_j = cj[l < nc ? l : 0];
+          // candidate m is in lane m: broadcast it with lane reads
+          const int my_lo = (int)(uint32_t)__double_as_longlong(my_s);
+          const int my_hi = (int)(uint32_t)(__double_as_longlong(my_s) >> 32);
+          int rank = 0;
+          for (int m = 0; m < nc; ++m) {
+            const uint64_t ob = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(my_hi, m) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane(my_lo, m);
+            const double os = __longlong_as_double((long long)ob);
+            const int oj = __builtin_amdgcn_readlane(my_j, m);
+            rank += (os > my_s || (os == my_s && oj < my_j)) ? 1 : 0;
+          }
+          const uint64_t last = __ballot(l < nc && rank == need - 1);
+          const int Ll = __ffsll((unsigned long long)last) - 1;
+          const double ts = __shfl(my_s, Ll);
+          const int tj = __shfl(my_j, Ll);
+#pragma unroll
+          for (int t = 0; t < NTP; ++t)
+            selm[t] |= __ballot(((cm[t] >> l) & 1ull) &&
+                                (s[t] > ts || (s[t] == ts && l + 64 * t <= tj)));
+          wave_sync();
+        } else {
+          // Many equal or nearly equal scores: exact fp64 order among the
+          // candidates by a bisection over their 64-bit order keys.
+          uint64_t k64[NTP];
+#pragma unroll
+          for (int t = 0; t < NTP; ++t)
+            k64[t] = ((cm[t] >> l) & 1ull) ? order64(s[t]) : 0ull;
+          uint64_t T2 = 0;
+          for (int bit = 63; bit >= 0; --bit) {
+            const uint64_t cand = T2 | (1ull << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int t = 0; t < NTP; ++t) cnt += __popcll(__ballot(k64[t] >= cand));
+            if (cnt >= need) T2 = cand;
+          }
+          int need2 = need;
+#pragma unroll
+          for (int t = 0; t < NTP; ++t) {
+            const uint64_t m = __ballot(k64[t] > T2);
+            selm[t] |= m;
+            need2 -= __popcll(m);
+          }
+          // ties at T2: ascending key index = slot-major, lane-minor
+          for (int t = 0; t < NTP; ++t) {
+            uint64_t tm = __ballot(k64[t] == T2);
+            while (need2 > 0 && tm) {
+              const uint64_t low = tm & (~tm + 1ull);
+              selm[t] |= low;
+              tm ^= low;
+              --need2;
+            }
           }
         }
-      }
+        if (CAUSAL) {  // the most recent keys lim..qr
+#pragma unroll
+          for (int t = 0; t < NTP; ++t)
+            selm[t] |= __ballot(l + 64 * t >= lim && l + 64 * t <= qr);
+        }
+      }  // !dense
       // compact the chosen (index, score) pairs in ascending index order
       int before = 0;
 #pragma unroll
@@ -352,6 +377,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
         }
         before += __popcll(mt);
       }
+      if (CAUSAL && idxg)  // rows keeping fewer than topk keys: pad with -1
+        for (int p = cnt + l; p < topk; p += 64) idxg[(bh * n + qr) * (size_t)topk + p] = -1;
     }
     // From here on every LDS word a wave touches is its own (row i of S and
     // its index list), so the lanes of the wave only need to see each other.
@@ -362,10 +389,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
       const int dq = l % 16;
       double acc[4] = {0.0, 0.0, 0.0, 0.0};
       // chunks of 64 selected keys: each slot group issues its 16 row loads
-      // before accumulating (one memory latency per chunk); slots past topk
-      // read row 0 and contribute nothing.
+      // before accumulating (one memory latency per chunk); slots past the
+      // row's key count read row 0 and contribute nothing.
       auto chunk = [&](int p0, auto full) {
-        constexpr bool FULL = decltype(full)::value;  // all 64 slots < topk
+        constexpr bool FULL = decltype(full)::value;  // all 64 slots < cnt
         float4 vv[16];
         double sj[16];
         int jr[16];
@@ -376,13 +403,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          const int j = (FULL || p0 + sg + 4 * u < topk) ? jr[u] : 0;
+          const int j = (FULL || p0 + sg + 4 * u < cnt) ? jr[u] : 0;
           vv[u] = *reinterpret_cast<const float4 *>(vb + (size_t)j * DIM + 4 * dq);
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          // a slot past topk adds fma(0, 0, acc) = acc exactly
-          const bool ok = FULL || p0 + sg + 4 * u < topk;
+          // a slot past cnt adds fma(0, 0, acc) = acc exactly
+          const bool ok = FULL || p0 + sg + 4 * u < cnt;
           const double sv = ok ? sj[u] : 0.0;
           const float4 x = ok ? vv[u] : float4{0.f, 0.f, 0.f, 0.f};
           acc[0] = fma(sv, (double)x.x, acc[0]);
@@ -392,8 +419,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
         }
       };
       int p0 = 0;
-      for (; p0 + 64 <= topk; p0 += 64) chunk(p0, std::true_type{});
-      if (p0 < topk) chunk(p0, std::false_type{});
+      for (; p0 + 64 <= cnt; p0 += 64) chunk(p0, std::true_type{});
+      if (p0 < cnt) chunk(p0, std::false_type{});
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         acc[e] += __shfl_xor(acc[e], 16);
@@ -408,31 +435,36 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
   }
 }
 
-template <int NTP>
+template <int NTP, bool CAUSAL>
 hipError_t launch_ntp(const TopkArgs &a, hipStream_t stream) {
   const size_t shmem = (size_t)64 * NTP * (QB * 8 + 4 * 4);
   if (shmem > 65536) {  // opt in to more than 64 KiB of LDS (gfx950: 160 KiB)
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&topk_kernel<NTP>),
+        reinterpret_cast<const void *>(&topk_kernel<NTP, CAUSAL>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     if (e != hipSuccess) return e;
   }
   const int n_qtiles = (a.n + QB - 1) / QB;
   const int n_work = n_qtiles * a.h * a.b;  // <= 2^23, checked by the caller
-  topk_kernel<NTP><<<n_work, kThreads, shmem, stream>>>(
+  topk_kernel<NTP, CAUSAL><<<n_work, kThreads, shmem, stream>>>(
       a.q, a.k, a.v, a.out, a.idx, a.n, a.topk, n_qtiles, n_work);
   return hipGetLastError();
+}
+
+template <bool CAUSAL>
+hipError_t launch_causal(const TopkArgs &a, hipStream_t stream) {
+  const int nt = (a.n + 63) / 64;
+  if (nt <= 1) return launch_ntp<1, CAUSAL>(a, stream);
+  if (nt <= 2) return launch_ntp<2, CAUSAL>(a, stream);
+  if (nt <= 4) return launch_ntp<4, CAUSAL>(a, stream);
+  if (nt <= 8) return launch_ntp<8, CAUSAL>(a, stream);
+  return launch_ntp<16, CAUSAL>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
-  const int nt = (a.n + 63) / 64;
-  if (nt <= 1) return launch_ntp<1>(a, stream);
-  if (nt <= 2) return launch_ntp<2>(a, stream);
-  if (nt <= 4) return launch_ntp<4>(a, stream);
-  if (nt <= 8) return launch_ntp<8>(a, stream);
-  return launch_ntp<16>(a, stream);
+  return a.causal ? launch_causal<true>(a, stream) : launch_causal<false>(a, stream);
 }
 
 }  // namespace attn
