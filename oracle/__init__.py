@@ -8,9 +8,12 @@ from .attention import (  # noqa: F401
     default_scale,
     decode,
     decode_append,
+    decode_append_rope,
     decode_paged,
     decode_sequence,
     prefill,
+    rope_rotate,
+    round_to_storage,
     topk_causal_select,
     topk_causal_sparse,
     topk_sparse,

@@ -174,6 +174,66 @@ def decode_paged(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray,
                   scale=scale)
 
 
+def rope_rotate(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotary position embedding of the last axis in float64, no rounding.
+
+    [P1 §4.1] applies ``apply_rotary_pos_emb(q, k, cos, sin)`` to the
+    current token's query and key before the cache write; the function body
+    is not on the page. Reading: the rotate-half convention, element j paired
+    with element j + D/2: out = x * cos + rotate_half(x) * sin with
+    rotate_half(x) = (-x[D/2:], x[:D/2]). ``cos`` and ``sin`` broadcast
+    against x (full length D).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    h = x.shape[-1] // 2
+    rh = np.concatenate([-x[..., h:], x[..., :h]], axis=-1)
+    return x * np.asarray(cos, np.float64) + rh * np.asarray(sin, np.float64)
+
+
+def round_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values once, to nearest even, to the storage type
+    ``dtype`` ("bf16": 8 significant bits, float32's exponent range; "f32"),
+    returned as float64."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    out = np.array(x, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    e = np.floor(np.log2(np.abs(x[fin])))
+    # guard log2 rounding at exact powers of two
+    e = np.where(np.abs(x[fin]) < 2.0 ** e, e - 1, e)
+    e = np.where(np.abs(x[fin]) >= 2.0 ** (e + 1), e + 1, e)
+    ulp = 2.0 ** (np.maximum(e, -126.0) - 7.0)
+    out[fin] = np.rint(x[fin] / ulp) * ulp
+    big = np.abs(out) > 3.3895313892515355e38    # beyond the largest bf16
+    out[big] = np.sign(out[big]) * np.inf
+    return out
+
+
+def decode_append_rope(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+                       cos: np.ndarray, sin: np.ndarray,
+                       k_cache: np.ndarray, v_cache: np.ndarray,
+                       dtype: str,
+                       position_id: Optional[int] = None,
+                       seq_lens: Optional[np.ndarray] = None,
+                       scale: Optional[float] = None):
+    """The patched ``forward_step`` with its position embedding [P1 §4.1]:
+    rotate the query and the new key (``rope_rotate``; ``cos``, ``sin``
+    [B, D] give sequence b's current position, shared by all heads), round
+    both to the storage type (reading: the rotated tensors are the model's
+    dtype, as SDPA and the cache receive them), then store and attend as in
+    ``decode_append``. Returns (out, k_cache', v_cache')."""
+    c = np.asarray(cos, np.float64)[:, None, :]
+    s = np.asarray(sin, np.float64)[:, None, :]
+    q_r = round_to_storage(rope_rotate(q, c, s), dtype)
+    k_r = round_to_storage(rope_rotate(k_new, c, s), dtype)
+    return decode_append(q_r, k_r, v_new, k_cache, v_cache,
+                         position_id=position_id, seq_lens=seq_lens,
+                         scale=scale)
+
+
 # ----------------------------------------------------------------------------
 # Causal prefill against a cached prefix  [P2 solution section]
 # ----------------------------------------------------------------------------

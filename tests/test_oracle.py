@@ -197,6 +197,123 @@ def test_decode_append_ragged_rows_and_empty_sequence():
                                rtol=0, atol=1e-15)
 
 
+def _rope_tables(positions, D, base=10000.0):
+    """Standard rotary tables: angle pos * base^(-2j/D) for pair j, the same
+    angle on elements j and j + D/2."""
+    inv = base ** (-np.arange(0, D, 2) / D)
+    ang = np.asarray(positions, np.float64)[:, None] * inv[None, :]
+    ang = np.concatenate([ang, ang], axis=-1)
+    return np.cos(ang), np.sin(ang)
+
+
+def test_rope_quarter_and_half_turns():
+    x = np.array([1.0, 2.0, 3.0, 4.0])
+    assert oracle.rope_rotate(x, np.zeros(4), np.ones(4)).tolist() == \
+        [-3.0, -4.0, 1.0, 2.0]
+    assert oracle.rope_rotate(x, -np.ones(4), np.zeros(4)).tolist() == \
+        [-1.0, -2.0, -3.0, -4.0]
+    assert oracle.rope_rotate(x, np.ones(4), np.zeros(4)).tolist() == \
+        x.tolist()
+
+
+def test_rope_is_complex_multiplication_of_half_pairs():
+    # element j and j + D/2 as the complex number x_j + i x_{j+D/2}, turned
+    # by e^{i theta_j}
+    rng = np.random.default_rng(60)
+    D = 16
+    x = rng.standard_normal((5, 3, D))
+    c, s = _rope_tables([0, 1, 7, 100, 4095], D)
+    got = oracle.rope_rotate(x, c[:, None, :], s[:, None, :])
+    z = (x[..., :D // 2] + 1j * x[..., D // 2:]) * \
+        np.exp(1j * np.arctan2(s, c)[:, None, :D // 2])
+    np.testing.assert_allclose(got, np.concatenate([z.real, z.imag], -1),
+                               rtol=0, atol=1e-13)
+
+
+def test_rope_scores_depend_on_the_position_difference_only():
+    rng = np.random.default_rng(61)
+    D = 32
+    q = rng.standard_normal(D)
+    k = rng.standard_normal(D)
+    pos = np.array([5, 2, 105, 102, 3000, 2997])
+    c, s = _rope_tables(pos, D)
+    qr = oracle.rope_rotate(q, c, s)
+    kr = oracle.rope_rotate(k, c, s)
+    d1 = qr[0] @ kr[1]
+    assert abs(qr[2] @ kr[3] - d1) < 1e-10
+    assert abs(qr[4] @ kr[5] - d1) < 1e-10
+    assert abs(q @ k - d1) > 1e-3  # the rotation does change the score
+
+
+def test_round_to_storage_bf16_ties_and_library_encoder():
+    one = 1.0
+    r = oracle.round_to_storage(np.array([one + 2.0 ** -8, one + 3 * 2.0 ** -8,
+                                          -(one + 2.0 ** -8 + 2.0 ** -30),
+                                          2.0 ** -130, 0.0, -0.0]), "bf16")
+    assert r[0] == 1.0                      # tie to even (down)
+    assert r[1] == 1.0 + 2.0 ** -6          # tie to even (up)
+    assert r[2] == -(1.0 + 2.0 ** -7)       # above the tie: away from 1
+    assert r[3] == 2.0 ** -130              # subnormal, exact
+    assert r[4] == 0.0 and np.signbit(r[5])
+    # against the bit-level float32 -> bf16 encoder on float32 values
+    rng = np.random.default_rng(62)
+    x = (rng.standard_normal(20000) *
+         np.exp(rng.uniform(-40, 40, 20000))).astype(np.float32)
+    ref = synth.bf16_to_f32(synth.f32_to_bf16_bits(x)).astype(np.float64)
+    np.testing.assert_array_equal(
+        oracle.round_to_storage(x.astype(np.float64), "bf16"), ref)
+
+
+def test_decode_append_rope_with_identity_tables_is_the_plain_append():
+    rng = np.random.default_rng(63)
+    B, Hq, Hkv, D, M = 3, 4, 2, 8, 10
+    enc = lambda a: synth.bf16_to_f32(synth.f32_to_bf16_bits(
+        a.astype(np.float32))).astype(np.float64)
+    q = enc(rng.standard_normal((B, Hq, D)))
+    kn = enc(rng.standard_normal((B, Hkv, D)))
+    vn = enc(rng.standard_normal((B, Hkv, D)))
+    k = enc(rng.standard_normal((B, Hkv, M, D)))
+    v = enc(rng.standard_normal((B, Hkv, M, D)))
+    lens = np.array([1, 10, 4])
+    a = oracle.decode_append(q, kn, vn, k, v, seq_lens=lens)
+    b = oracle.decode_append_rope(q, kn, vn, np.ones((B, D)),
+                                  np.zeros((B, D)), k, v, "bf16",
+                                  seq_lens=lens)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("p", [0, 6])
+def test_decode_append_rope_follows_the_page_forward_step(p):
+    # [P1 §4.1]: rotate q and k, store k (and v) at position_id, SDPA over
+    # [0, position_id]. Rotation by complex multiplication, rounding to
+    # float32 by numpy, attention by torch's SDPA.
+    rng = np.random.default_rng(64 + p)
+    B, Hq, Hkv, D, M = 2, 4, 2, 8, 9
+    f = lambda a: a.astype(np.float32).astype(np.float64)
+    q = f(rng.standard_normal((B, Hq, D)))
+    kn = f(rng.standard_normal((B, Hkv, D)))
+    vn = f(rng.standard_normal((B, Hkv, D)))
+    k = f(rng.standard_normal((B, Hkv, M, D)))
+    v = f(rng.standard_normal((B, Hkv, M, D)))
+    k[:, :, p] = np.nan
+    c, s = _rope_tables([p, p], D)
+    out, k2, v2 = oracle.decode_append_rope(q, kn, vn, c, s, k, v, "f32",
+                                            position_id=p)
+    th = np.arctan2(s, c)[:, None, :D // 2]
+    turn = lambda a: (lambda z: np.concatenate([z.real, z.imag], -1))(
+        (a[..., :D // 2] + 1j * a[..., D // 2:]) * np.exp(1j * th))
+    qr, kr = f(turn(q)), f(turn(kn))
+    kt = np.array(k, copy=True)
+    kt[:, :, p] = kr
+    vt = np.array(v, copy=True)
+    vt[:, :, p] = vn
+    ref = _sdpa_sliced(qr, kt, vt, p + 1)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(k2, kt)
+    np.testing.assert_array_equal(v2, vt)
+
+
 def test_decode_paged_equals_contiguous_and_sdpa():
     # a contiguous cache scattered over shuffled token-major pages (spare
     # pages hold NaN): the paged oracle must see exactly the same rows
