@@ -220,25 +220,40 @@ def bench_append(torch, tas, dec, steps):
     out = torch.empty_like(dec["out"])
     kw = dict(seq_lens=dec["seq_lens"], scale=p["scale"], out=out,
               workspace=dec["ws"])
+    # rotary tables of each sequence's current row (rotate-half layout)
+    rows = torch.clamp(dec["seq_lens"].long() - 1, min=0).double()
+    inv = 10000.0 ** (-torch.arange(0, D, 2, device="cuda").double() / D)
+    ang = rows[:, None] * inv[None, :]
+    ang = torch.cat([ang, ang], dim=-1)
+    cos, sin = ang.cos().float().contiguous(), ang.sin().float().contiguous()
+    calls = (
+        lambda: tas.attn_decode_append(dec["q"], k_new, v_new, dec["k"],
+                                       dec["v"], **kw),
+        lambda: tas.attn_decode_append_rope(dec["q"], k_new, v_new, cos, sin,
+                                            dec["k"], dec["v"], **kw),
+        lambda: tas.attn_decode(dec["q"], dec["k"], dec["v"], **kw),
+    )
     for _ in range(5):
-        tas.attn_decode_append(dec["q"], k_new, v_new, dec["k"], dec["v"], **kw)
-        tas.attn_decode(dec["q"], dec["k"], dec["v"], **kw)
+        for c in calls:
+            c()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
           for _ in range(steps)]
     for e in ev:
-        e[0].record()
-        tas.attn_decode_append(dec["q"], k_new, v_new, dec["k"], dec["v"], **kw)
-        e[1].record()
-        tas.attn_decode(dec["q"], dec["k"], dec["v"], **kw)
-        e[2].record()
+        for i, c in enumerate(calls):
+            e[i].record()
+            c()
+        e[3].record()
     torch.cuda.synchronize()
-    ta = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in ev]))
-    td = float(np.median([e[1].elapsed_time(e[2]) * 1e3 for e in ev]))
+    ta, tr, td = (float(np.median([e[i].elapsed_time(e[i + 1]) * 1e3
+                                   for e in ev])) for i in range(3))
     return dict(workload="decode_ragged_b64 + append of one row per "
                          "(sequence, kv head)",
-                us_p50_append_decode=round(ta, 2), us_p50_decode=round(td, 2),
-                GBps_append_decode=round(dec["bytes"] / (ta * 1e-6) / 1e9, 1))
+                us_p50_append_decode=round(ta, 2),
+                us_p50_rope_append_decode=round(tr, 2),
+                us_p50_decode=round(td, 2),
+                GBps_append_decode=round(dec["bytes"] / (ta * 1e-6) / 1e9, 1),
+                GBps_rope_append_decode=round(dec["bytes"] / (tr * 1e-6) / 1e9, 1))
 
 
 def bench_paged(torch, tas, dec, steps, page_size, layout):
@@ -502,7 +517,7 @@ def main():
     traffic = committed_traffic("decode_ragged_b64_traffic.txt",
                                 "decode.hip")
     roofline = {
-        "kernel": "decode_bf16_kernel<128,4,false> + decode_combine_kernel<true,128> (one attn_decode call)",
+        "kernel": "decode_bf16_kernel<128, 4, 0> + decode_combine_kernel<true, 128> (one attn_decode call)",
         "bound": "hbm", "achieved": round(dec_gbps, 1),
         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),

@@ -1,9 +1,9 @@
 /*
  * attn.h — C ABI of the MI355X (gfx950) KV-cache attention library.
  *
- * Three operations (plus decode with a fused cache append and decode over a
- * paged cache), each one asynchronous launch sequence on the caller's HIP
- * stream:
+ * Three operations (plus decode with a fused cache append, with or without
+ * the rotary embedding, decode over a paged cache and the decoder form of
+ * top-k), each one asynchronous launch sequence on the caller's HIP stream:
  *
  *   attn_decode   single-token decode over a statically preallocated cache,
  *                 attending to rows [0, position_id] (or [0, seq_lens[b]) for
@@ -155,6 +155,33 @@ int attn_decode_append(int dtype, const void *q, const void *k_new,
                        int position_id, const int32_t *seq_lens, float scale,
                        int split_rows, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/* Fused rotary embedding + append + decode. The patched forward_step of
+ * "MiniCPM4 forward_step Attention Performance Fix" (§4.1) rotates the
+ * current token's query and key with its position embedding (cos, sin) by
+ * apply_rotary_pos_emb before the cache write and the attention; the page
+ * does not spell that function out. This call uses the rotate-half
+ * convention: for each head's row x of length D, element j is paired with
+ * j + D/2 and
+ *   x'_j = x_j·cos_j − x_{j+D/2}·sin_j        (j < D/2)
+ *   x'_j = x_j·cos_j + x_{j−D/2}·sin_j        (j ≥ D/2),
+ * computed in fp32 and rounded once to the storage type.
+ *
+ *   rope_cos,
+ *   rope_sin   fp32 [B][D], 16-byte aligned: the cos / sin row of sequence
+ *              b's current position (the same for every head); not modified.
+ * q and k_new[b] are rotated with row b; k_cache row r_b receives the rotated
+ * key and v_new unchanged, and the rotated query attends. Everything else is
+ * attn_decode_append. ATTN_E_ARG if B > 0 and a table pointer is NULL or
+ * misaligned. */
+int attn_decode_append_rope(int dtype, const void *q, const void *k_new,
+                            const void *v_new, const float *rope_cos,
+                            const float *rope_sin, void *k_cache, void *v_cache,
+                            void *out, int B, int Hq, int Hkv, int D,
+                            int max_length, int position_id,
+                            const int32_t *seq_lens, float scale, int split_rows,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /* Page layouts of attn_decode_paged. */
 typedef enum attn_page_layout {

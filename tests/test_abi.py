@@ -140,6 +140,42 @@ def test_decode_append_batch_zero_is_a_noop():
     assert decode_append(B=0, kn=None, vn=None, ws=None, ws_bytes=0) == OK
 
 
+def decode_append_rope(**kw):
+    a = dict(dtype=BF16, q=P, kn=P, vn=P, cos=P, sin=P, k=P, v=P, out=P, B=1,
+             Hq=32, Hkv=8, D=128, max_length=8192, position_id=100,
+             seq_lens=None, scale=0.088, split_rows=0, ws=P, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.attn_decode_append_rope(
+        a["dtype"], a["q"], a["kn"], a["vn"], a["cos"], a["sin"], a["k"],
+        a["v"], a["out"], a["B"], a["Hq"], a["Hkv"], a["D"], a["max_length"],
+        a["position_id"], a["seq_lens"], a["scale"], a["split_rows"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cos=None), E_ARG),
+    (dict(sin=None), E_ARG),
+    (dict(cos=P + 4), E_ARG),
+    (dict(sin=P + 8), E_ARG),
+    (dict(kn=None), E_ARG),
+    (dict(vn=P + 2), E_ARG),
+    (dict(dtype=7), E_ARG),
+    (dict(D=96), E_UNSUP),
+    (dict(Hq=24, Hkv=8), E_UNSUP),
+    (dict(position_id=-1), E_ARG),
+    (dict(ws_bytes=16), E_WS),
+])
+def test_decode_append_rope_rejects(kw, status):
+    assert decode_append_rope(**kw) == status
+    assert lib.attn_last_error().decode().startswith("attn_decode_append_rope")
+
+
+def test_decode_append_rope_batch_zero_is_a_noop():
+    assert decode_append_rope(B=0, kn=None, vn=None, cos=None, sin=None,
+                              ws=None, ws_bytes=0) == OK
+
+
 def decode_paged(**kw):
     a = dict(dtype=BF16, q=P, kp=P, vp=P, bt=P, max_blocks=64, page_size=128,
              num_pages=100, layout=0, out=P, B=1, Hq=32, Hkv=8, D=128,

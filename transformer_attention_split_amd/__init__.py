@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     attn_decode,
     attn_decode_append,
+    attn_decode_append_rope,
     attn_decode_paged,
     attn_decode_workspace_bytes,
     attn_prefill,
@@ -24,6 +25,7 @@ from ._binding import (  # noqa: F401
     lib,
 )
 
-__all__ = ["attn_decode", "attn_decode_append", "attn_decode_paged",
+__all__ = ["attn_decode", "attn_decode_append", "attn_decode_append_rope",
+           "attn_decode_paged",
            "attn_prefill", "attn_topk", "attn_topk_causal",
            "attn_decode_workspace_bytes", "AttnError", "AttnArgError"]

@@ -48,6 +48,10 @@ lib.attn_decode.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p,
 lib.attn_decode_append.restype = _i
 lib.attn_decode_append.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i,
                                    _i, _i, _p, _f, _i, _p, _sz, _p]
+lib.attn_decode_append_rope.restype = _i
+lib.attn_decode_append_rope.argtypes = [_i, _p, _p, _p, _p, _p, _p, _p, _p, _i,
+                                        _i, _i, _i, _i, _i, _p, _f, _i, _p,
+                                        _sz, _p]
 lib.attn_decode_paged.restype = _i
 lib.attn_decode_paged.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _i,
                                   _i, _i, _i, _i, _p, _f, _i, _p, _sz, _p]
@@ -61,6 +65,7 @@ lib.attn_topk_causal.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 
 EXPORTED = ("attn_status_str", "attn_last_error", "attn_abi_version",
             "attn_decode_workspace_bytes", "attn_decode", "attn_decode_append",
+            "attn_decode_append_rope",
             "attn_decode_paged", "attn_prefill", "attn_topk",
             "attn_topk_causal")
 
@@ -208,6 +213,41 @@ def attn_decode_append(q: torch.Tensor, k_new: torch.Tensor,
         scale, int(split_rows), _ptr(workspace), workspace.numel(),
         _stream_handle(stream))
     _check(st, "attn_decode_append")
+    return out
+
+
+def attn_decode_append_rope(q: torch.Tensor, k_new: torch.Tensor,
+                            v_new: torch.Tensor, cos: torch.Tensor,
+                            sin: torch.Tensor, k_cache: torch.Tensor,
+                            v_cache: torch.Tensor, *,
+                            position_id: Optional[int] = None,
+                            seq_lens: Optional[torch.Tensor] = None,
+                            scale: Optional[float] = None, split_rows: int = 0,
+                            out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """Rotary embedding + append + decode: q and k_new are rotated with the
+    fp32 cos / sin rows [B,D] of each sequence's current position
+    (rotate-half pairs j, j+D/2), the rotated key and v_new are stored as in
+    ``attn_decode_append`` and the rotated query attends."""
+    B, Hq, Hkv, D, max_length, scale, out, workspace = _decode_args(
+        q, k_cache, v_cache, position_id, seq_lens, scale, split_rows, out,
+        workspace)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need_dense(name, t, 3)
+        if tuple(t.shape) != (B, Hkv, D) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [{B},{Hkv},{D}] {q.dtype}")
+    for name, t in (("cos", cos), ("sin", sin)):
+        _need_dense(name, t, 2)
+        if tuple(t.shape) != (B, D) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [{B},{D}]")
+    st = lib.attn_decode_append_rope(
+        _dtype_code(q), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cos),
+        _ptr(sin), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, Hq, Hkv, D,
+        max_length, -1 if position_id is None else int(position_id),
+        _ptr(seq_lens), scale, int(split_rows), _ptr(workspace),
+        workspace.numel(), _stream_handle(stream))
+    _check(st, "attn_decode_append_rope")
     return out
 
 

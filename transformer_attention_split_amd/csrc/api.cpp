@@ -238,13 +238,16 @@ int decode_impl(const char *fn, int dtype, const void *q, const void *k_new,
                 void *out, int B, int Hq, int Hkv, int D, int max_length,
                 int position_id, const int32_t *seq_lens, float scale,
                 int split_rows, void *workspace, size_t workspace_bytes,
-                void *stream) {
+                void *stream, const float *rope_cos = nullptr,
+                const float *rope_sin = nullptr) {
   attn::DecodeArgs a;
   const int st = decode_check(fn, dtype, q, k_new, v_new, k_cache, v_cache,
                               out, B, Hq, Hkv, D, max_length, position_id,
                               seq_lens, scale, split_rows, workspace,
                               workspace_bytes, 1, a);
   if (st != ATTN_OK || a.B == 0) return st;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
   hipError_t e = attn::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
@@ -277,6 +280,25 @@ int attn_decode_append(int dtype, const void *q, const void *k_new,
                      v_cache, out, B, Hq, Hkv, D, max_length, position_id,
                      seq_lens, scale, split_rows, workspace, workspace_bytes,
                      stream);
+}
+
+int attn_decode_append_rope(int dtype, const void *q, const void *k_new,
+                            const void *v_new, const float *rope_cos,
+                            const float *rope_sin, void *k_cache, void *v_cache,
+                            void *out, int B, int Hq, int Hkv, int D,
+                            int max_length, int position_id,
+                            const int32_t *seq_lens, float scale, int split_rows,
+                            void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  const char *fn = "attn_decode_append_rope";
+  if (B > 0 && (!k_new || !v_new || !rope_cos || !rope_sin))
+    return fail(ATTN_E_ARG, "%s: null k_new / v_new / rope_cos / rope_sin", fn);
+  if (B > 0 && (!aligned(rope_cos, 16) || !aligned(rope_sin, 16)))
+    return fail(ATTN_E_ARG, "%s: rope_cos / rope_sin must be 16-byte aligned", fn);
+  return decode_impl(fn, dtype, q, k_new, v_new, k_cache, v_cache, out, B, Hq,
+                     Hkv, D, max_length, position_id, seq_lens, scale,
+                     split_rows, workspace, workspace_bytes, stream, rope_cos,
+                     rope_sin);
 }
 
 

@@ -66,6 +66,42 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// Rotary position embedding, rotate-half convention: element j of a row is
+// paired with j + D/2, out_j = x_j·cos_j + r_j·sin_j with r_j = -x_{j+D/2}
+// for j < D/2 and x_{j-D/2} otherwise; fp32, one fma per element.
+// rope_bf16x8: x = 8 bf16 elements j0..j0+7, p = their partners, c / s the
+// cos / sin values of j0..j0+7, lo = (j0 < D/2); one rounding to bf16.
+__device__ __forceinline__ float rope1(float x, float p, float c, float s, bool lo) {
+  return fmaf(x, c, (lo ? -p : p) * s);
+}
+__device__ __forceinline__ u32x4_t rope_bf16x8(u32x4_t x, u32x4_t p, const float *c,
+                                               const float *s, bool lo) {
+  const float4 c0 = *reinterpret_cast<const float4 *>(c);
+  const float4 c1 = *reinterpret_cast<const float4 *>(c + 4);
+  const float4 s0 = *reinterpret_cast<const float4 *>(s);
+  const float4 s1 = *reinterpret_cast<const float4 *>(s + 4);
+  const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  u32x4_t r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    r[w] = pack_bf16x2(rope1(bf16lo(x[w]), bf16lo(p[w]), cc[2 * w], ss[2 * w], lo),
+                       rope1(bf16hi(x[w]), bf16hi(p[w]), cc[2 * w + 1], ss[2 * w + 1], lo));
+  return r;
+}
+// the same for 4 fp32 elements (no rounding)
+__device__ __forceinline__ u32x4_t rope_f32x4(u32x4_t x, u32x4_t p, const float *c,
+                                              const float *s, bool lo) {
+  const float4 cv = *reinterpret_cast<const float4 *>(c);
+  const float4 sv = *reinterpret_cast<const float4 *>(s);
+  const float cc[4] = {cv.x, cv.y, cv.z, cv.w}, ss[4] = {sv.x, sv.y, sv.z, sv.w};
+  u32x4_t r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    r[e] = __float_as_uint(rope1(__uint_as_float(x[e]), __uint_as_float(p[e]), cc[e], ss[e], lo));
+  return r;
+}
+
 struct Item {
   int L;        // valid rows of the sequence
   int row0;     // first row of this split
@@ -213,7 +249,8 @@ struct Bf16Tile {
 };
 
 // MODE: 0 = contiguous cache, 1 = contiguous cache with the fused append,
-// 2 = paged cache.
+// 2 = paged cache, 3 = fused append with the rotary embedding of the query
+// and the new key.
 template <int D, int G, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     const uint16_t *__restrict__ qg, const uint16_t *__restrict__ kg,
@@ -223,9 +260,11 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     int max_length, int split_rows, int splits, float qk_scale,
     const uint16_t *__restrict__ knew, const uint16_t *__restrict__ vnew,
     uint16_t *kw, uint16_t *vw, const int32_t *__restrict__ block_table,
-    int max_blocks, int page_size, int num_pages, int head_major) {
-  constexpr bool APPEND = MODE == 1;
+    int max_blocks, int page_size, int num_pages, int head_major,
+    const float *__restrict__ rcos, const float *__restrict__ rsin) {
+  constexpr bool APPEND = MODE == 1 || MODE == 3;
   constexpr bool PAGED = MODE == 2;
+  constexpr bool ROPE = MODE == 3;
   using T = Bf16Tile<D>;
   constexpr int BN = T::BN, KS = T::KS, NDB = T::NDB, NKB = T::NKB;
   constexpr int SV = T::SV;
@@ -234,6 +273,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   constexpr int LDS_BYTES = LDS_MAIN > LDS_FIN ? LDS_MAIN : LDS_FIN;
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
   __shared__ float fin_m[G], fin_l[G];
+  __shared__ __attribute__((aligned(16))) uint16_t krot[ROPE ? D : 8];  // rotated new key
 
   const Unit un = locate_unit(seq_lens, gridDim.y, Hkv, max_length, split_rows);
   if (un.b < 0) return;
@@ -252,16 +292,35 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   const int lg = l / 16;   // lane group (k slots 8*lg..8*lg+7)
 
   // Query heads of the group as the B operand of Sᵀ = K·Qᵀ (column li).
+  // Rotary embedding: chunk ks of a lane (elements ks*32 + 8*lg ...) pairs
+  // with chunk ks + KS/2 of the same lane (D/2 further on).
+  // (the rotation waits for the tables; it is made after the first tile's
+  // loads are issued so that their latency overlaps it)
   bf16x8_t qf[KS];
+  u32x4_t qv[KS];
   {
     const uint16_t *qrow = qg + ((size_t)b * Hq + (size_t)g * G + li) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (li < G) v = *reinterpret_cast<const u32x4_t *>(qrow + ks * 32 + 8 * lg);
-      qf[ks] = as_bf16x8(v);
+      qv[ks] = u32x4_t{0u, 0u, 0u, 0u};
+      if (li < G) qv[ks] = *reinterpret_cast<const u32x4_t *>(qrow + ks * 32 + 8 * lg);
+      qf[ks] = as_bf16x8(qv[ks]);
     }
   }
+  auto rotate_q = [&]() {
+    if (li < G) {
+      const float *cb = rcos + (size_t)b * D, *sb = rsin + (size_t)b * D;
+#pragma unroll
+      for (int ks = 0; ks < KS / 2; ++ks) {
+        const int j0 = ks * 32 + 8 * lg;
+        const u32x4_t lo = qv[ks], hi = qv[ks + KS / 2];
+        qv[ks] = rope_bf16x8(lo, hi, cb + j0, sb + j0, true);
+        qv[ks + KS / 2] = rope_bf16x8(hi, lo, cb + j0 + D / 2, sb + j0 + D / 2, false);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(qv[ks]);
+  };
 
   const size_t kvbase = ((size_t)b * Hkv + g) * (size_t)max_length * D;
   const uint16_t *kb = kg + kvbase;
@@ -289,17 +348,31 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   };
   // Appending: the sequence's last valid row is the new token. Its K and V
   // are read from knew / vnew (so no workgroup reads that cache row while it
-  // is being written) and split 0 stores them into the cache.
+  // is being written) and split 0 stores them into the cache. With the rotary
+  // embedding split 0 and the workgroup whose split holds the new row rotate
+  // the new key (into LDS, krot, for the latter); the wave whose tile holds
+  // the new row takes that row's K from there.
   const int arow = APPEND ? it.L - 1 : -1;
   const uint16_t *kn = knew + ((size_t)b * Hkv + g) * D;
   const uint16_t *vn = vnew + ((size_t)b * Hkv + g) * D;
-  if (APPEND && s == 0) {
+  const bool holds_arow = ROPE && it.row0 <= arow && arow < it.row1;  // uniform
+  if (APPEND && (s == 0 || holds_arow)) {
     for (int i = tid; i < D / 8; i += kThreads) {
-      *reinterpret_cast<u32x4_t *>(kw + kvbase + (size_t)arow * D + 8 * i) =
-          *reinterpret_cast<const u32x4_t *>(kn + 8 * i);
-      *reinterpret_cast<u32x4_t *>(vw + kvbase + (size_t)arow * D + 8 * i) =
-          *reinterpret_cast<const u32x4_t *>(vn + 8 * i);
+      u32x4_t kx = *reinterpret_cast<const u32x4_t *>(kn + 8 * i);
+      if constexpr (ROPE) {
+        const int j0 = 8 * i;
+        const bool lo = j0 < D / 2;
+        const u32x4_t px = *reinterpret_cast<const u32x4_t *>(kn + (lo ? j0 + D / 2 : j0 - D / 2));
+        kx = rope_bf16x8(kx, px, rcos + (size_t)b * D + j0, rsin + (size_t)b * D + j0, lo);
+        if (holds_arow) *reinterpret_cast<u32x4_t *>(&krot[j0]) = kx;
+      }
+      if (s == 0) {
+        *reinterpret_cast<u32x4_t *>(kw + kvbase + (size_t)arow * D + 8 * i) = kx;
+        *reinterpret_cast<u32x4_t *>(vw + kvbase + (size_t)arow * D + 8 * i) =
+            *reinterpret_cast<const u32x4_t *>(vn + 8 * i);
+      }
     }
+    if (holds_arow) __syncthreads();  // krot complete (uniform over the workgroup)
   }
   uint16_t *vt = reinterpret_cast<uint16_t *>(smem + w * T::VT_BYTES);
   const int oct = l % T::NOCT;  // V transpose item: rows 8*oct..8*oct+7
@@ -341,6 +414,17 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   };
   auto compute_tile = [&](int t0, int tnext, int pgnext) {
     const bool full = t0 + BN <= it.row1;
+    if constexpr (ROPE) {
+      if (t0 <= arow && arow < t0 + BN) {  // this tile holds the new token
+#pragma unroll
+        for (int kb16 = 0; kb16 < NKB; ++kb16)
+          if (t0 + kb16 * 16 + li == arow) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              kf[kb16][ks] = *reinterpret_cast<const u32x4_t *>(&krot[ks * 32 + 8 * lg]);
+          }
+      }
+    }
     // ---- Sᵀ = K·Qᵀ --------------------------------------------------------------
     f32x4_t sc[NKB];
 #pragma unroll
@@ -427,6 +511,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
       const int pg0 = PAGED ? page_of(t0) : 0;
       load_k(t0, pg0);
       load_v(t0, pg0);
+      if constexpr (ROPE) rotate_q();
     }
     const int t1 = t0 + 4 * BN;
     // (the next tile's page is looked up before this tile's products, so the
@@ -489,7 +574,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
 // ---------------------------------------------------------------------------
 // fp32: vector-ALU form
 // ---------------------------------------------------------------------------
-template <int D, int G, bool APPEND>
+template <int D, int G, bool APPEND, bool ROPE>
 __global__ __launch_bounds__(kThreads) void decode_f32_kernel(
     const float *__restrict__ qp, const float *__restrict__ kp,
     const float *__restrict__ vp, const int32_t *__restrict__ seq_lens,
@@ -497,7 +582,8 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(
     float *__restrict__ ws_o, int Hq, int Hkv,
     int max_length, int split_rows, int splits, float qscale,
     const float *__restrict__ knew, const float *__restrict__ vnew,
-    float *kw, float *vw) {
+    float *kw, float *vw, const float *__restrict__ rcos,
+    const float *__restrict__ rsin) {
   constexpr int VEC = 4;                // floats per 16-byte chunk
   constexpr int LPR = D / VEC;          // lanes per cache row (16 or 32)
   constexpr int NG = kThreads / LPR;    // row groups per workgroup
@@ -519,15 +605,20 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(
   const int lr = tid % LPR;
   const int grp = tid / LPR;
 
+  // Rotary embedding: lane lr's elements pair with those of lane lr ± LPR/2
+  // (D/2 away), read again from memory.
+  const bool rlo = lr < LPR / 2;
+  const int rpart = (lr * VEC + D / 2) % D;
   float qv[G][VEC];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float4 x = *reinterpret_cast<const float4 *>(
-        qp + ((size_t)b * Hq + (size_t)g * G + h) * D + lr * VEC);
-    qv[h][0] = x.x * qscale;
-    qv[h][1] = x.y * qscale;
-    qv[h][2] = x.z * qscale;
-    qv[h][3] = x.w * qscale;
+    const float *qrow = qp + ((size_t)b * Hq + (size_t)g * G + h) * D;
+    u32x4_t x = *reinterpret_cast<const u32x4_t *>(qrow + lr * VEC);
+    if constexpr (ROPE)
+      x = rope_f32x4(x, *reinterpret_cast<const u32x4_t *>(qrow + rpart),
+                     rcos + (size_t)b * D + lr * VEC, rsin + (size_t)b * D + lr * VEC, rlo);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qv[h][e] = __uint_as_float(x[e]) * qscale;
   }
   float m[G], l[G], o[G][VEC];
 #pragma unroll
@@ -541,13 +632,19 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(
   const float *kb = kp + rowbase * D + lr * VEC;
   const float *vb = vp + rowbase * D + lr * VEC;
   // Appending: as in the bf16 kernel, the last valid row is read from knew /
-  // vnew and split 0 stores it into the cache.
+  // vnew and split 0 stores it into the cache; with the rotary embedding the
+  // rotated key chunk is kept in registers (knr).
   const int arow = APPEND ? it.L - 1 : -1;
   const float *kn = knew + ((size_t)b * Hkv + g) * D + lr * VEC;
   const float *vn = vnew + ((size_t)b * Hkv + g) * D + lr * VEC;
+  u32x4_t knr = {0u, 0u, 0u, 0u};
+  if constexpr (ROPE)
+    knr = rope_f32x4(*reinterpret_cast<const u32x4_t *>(kn),
+                     *reinterpret_cast<const u32x4_t *>(knew + ((size_t)b * Hkv + g) * D + rpart),
+                     rcos + (size_t)b * D + lr * VEC, rsin + (size_t)b * D + lr * VEC, rlo);
   if (APPEND && s == 0 && tid < LPR) {
     *reinterpret_cast<u32x4_t *>(kw + (rowbase + arow) * D + lr * VEC) =
-        *reinterpret_cast<const u32x4_t *>(kn);
+        ROPE ? knr : *reinterpret_cast<const u32x4_t *>(kn);
     *reinterpret_cast<u32x4_t *>(vw + (rowbase + arow) * D + lr * VEC) =
         *reinterpret_cast<const u32x4_t *>(vn);
   }
@@ -560,7 +657,10 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(
       kr[u] = u32x4_t{0u, 0u, 0u, 0u};
       vr[u] = kr[u];
       if (rr < it.row1) {
-        kr[u] = ldnt(APPEND && rr == arow ? kn : kb + (size_t)rr * D);
+        if (ROPE && rr == arow)
+          kr[u] = knr;
+        else
+          kr[u] = ldnt(APPEND && rr == arow ? kn : kb + (size_t)rr * D);
         vr[u] = ldnt(APPEND && rr == arow ? vn : vb + (size_t)rr * D);
       }
     }
@@ -754,22 +854,26 @@ void launch_split(const DecodeArgs &a, hipStream_t stream) {
         a.plan.split_rows, a.plan.splits, a.scale * kLog2e,
         static_cast<const uint16_t *>(a.k_new), static_cast<const uint16_t *>(a.v_new),
         static_cast<uint16_t *>(a.k_w), static_cast<uint16_t *>(a.v_w),
-        a.block_table, a.max_blocks, a.page_size, a.num_pages, a.head_major);
+        a.block_table, a.max_blocks, a.page_size, a.num_pages, a.head_major,
+        a.rope_cos, a.rope_sin);
   } else {
     static_assert(MODE != 2, "paged caches are bf16 only");
-    decode_f32_kernel<D, G, MODE == 1><<<grid, kThreads, 0, stream>>>(
+    decode_f32_kernel<D, G, MODE == 1 || MODE == 3, MODE == 3><<<grid, kThreads, 0, stream>>>(
         static_cast<const float *>(a.q), static_cast<const float *>(a.k),
         static_cast<const float *>(a.v), a.seq_lens, a.position_id, a.out,
         a.ws_ml, a.ws_o, a.Hq, a.Hkv, a.max_length,
         a.plan.split_rows, a.plan.splits, a.scale * kLog2e,
         static_cast<const float *>(a.k_new), static_cast<const float *>(a.v_new),
-        static_cast<float *>(a.k_w), static_cast<float *>(a.v_w));
+        static_cast<float *>(a.k_w), static_cast<float *>(a.v_w), a.rope_cos,
+        a.rope_sin);
   }
 }
 
 template <bool BF16, int D, int G>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
-  if (a.k_new != nullptr)
+  if (a.k_new != nullptr && a.rope_cos != nullptr)
+    launch_split<BF16, D, G, 3>(a, stream);
+  else if (a.k_new != nullptr)
     launch_split<BF16, D, G, 1>(a, stream);
   else if constexpr (BF16) {
     if (a.block_table != nullptr)

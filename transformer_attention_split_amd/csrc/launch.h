@@ -35,6 +35,9 @@ struct DecodeArgs {
   // (the same memory as k / v) and attended to in the same launch.
   const void *k_new = nullptr, *v_new = nullptr;
   void *k_w = nullptr, *v_w = nullptr;
+  // Rotary embedding in the fused append (null: none): fp32 [B][D] cos / sin
+  // rows of each sequence's current position, applied to q and k_new.
+  const float *rope_cos = nullptr, *rope_sin = nullptr;
   // Paged caches (bf16 only; null for a contiguous cache): k / v are
   // [num_pages][page_size][Hkv][D] (or head-major, below); block_table [B][max_blocks] gives the page
   // of every page_size rows of each sequence; max_length = max_blocks *
