@@ -304,6 +304,53 @@ def bench_paged(torch, tas, dec, steps, page_size, layout):
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the decode workload
 # ----------------------------------------------------------------------------
+def bench_prefill_paged(torch, tas, pre, page_size, layout, n=20):
+    """attn_prefill_paged on the prefill workload's cache cut into shuffled
+    pages of `page_size` rows, against attn_prefill on the contiguous cache:
+    n back-to-back calls of each between two events."""
+    p = pre["p"]
+    B, Hkv, D, M = p["B"], p["Hkv"], p["D"], p["max_length"]
+    nb = M // page_size
+    g = torch.Generator(device="cpu").manual_seed(4322)
+    table = torch.randperm(B * nb, generator=g).to(torch.int32).view(B, nb).cuda()
+    perm_dims = (0, 2, 3, 1, 4) if layout == "token" else (0, 2, 1, 3, 4)
+    src_k = pre["k"].view(B, Hkv, nb, page_size, D).permute(*perm_dims)
+    src_v = pre["v"].view(B, Hkv, nb, page_size, D).permute(*perm_dims)
+    kp = torch.empty((B * nb,) + tuple(src_k.shape[2:]), dtype=torch.bfloat16,
+                     device="cuda")
+    vp = torch.empty_like(kp)
+    idx = table.view(-1).long()
+    kp[idx] = src_k.reshape(kp.shape)
+    vp[idx] = src_v.reshape(vp.shape)
+    out = torch.empty_like(pre["out"])
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+    tp = timed(lambda: tas.attn_prefill_paged(
+        pre["q"], kp, vp, table, prefix_len=p["prefix_len"], layout=layout,
+        scale=p["scale"], out=out))
+    tc = timed(lambda: tas.attn_prefill(
+        pre["q"], pre["k"], pre["v"], prefix_len=p["prefix_len"],
+        scale=p["scale"], out=out))
+    del kp, vp
+    torch.cuda.empty_cache()
+    return dict(workload=f"prefill_prefix3072 in shuffled {page_size}-row "
+                         f"{layout}-major pages",
+                us_back_to_back_paged=round(tp, 2),
+                us_back_to_back_contiguous=round(tc, 2),
+                TFLOPs_paged=round(pre["flops"] / tp / 1e6, 1))
+
+
 def cpu_baseline(dec, synth, budget_s):
     import numpy as np
     import oracle
@@ -508,6 +555,10 @@ def main():
         log("paged decode on the ragged batch ...")
         secondary["decode_paged_ragged_b64"] = [
             bench_paged(torch, tas, dec, args.steps, ps, lay)
+            for lay in ("token", "head") for ps in (64, 256)]
+        log("paged prefill ...")
+        secondary["prefill_paged_prefix3072"] = [
+            bench_prefill_paged(torch, tas, pre, ps, lay)
             for lay in ("token", "head") for ps in (64, 256)]
     if not args.no_secondary:
         log("single-sequence position-8000 decode (graph replay) ...")

@@ -2,8 +2,9 @@
  * attn.h — C ABI of the MI355X (gfx950) KV-cache attention library.
  *
  * Three operations (plus decode with a fused cache append, with or without
- * the rotary embedding, decode over a paged cache and the decoder form of
- * top-k), each one asynchronous launch sequence on the caller's HIP stream:
+ * the rotary embedding, decode and prefill over a paged cache and the decoder
+ * form of top-k), each one asynchronous launch sequence on the caller's HIP
+ * stream:
  *
  *   attn_decode   single-token decode over a statically preallocated cache,
  *                 attending to rows [0, position_id] (or [0, seq_lens[b]) for
@@ -183,7 +184,7 @@ int attn_decode_append_rope(int dtype, const void *q, const void *k_new,
                             void *workspace, size_t workspace_bytes,
                             void *stream);
 
-/* Page layouts of attn_decode_paged. */
+/* Page layouts of attn_decode_paged and attn_prefill_paged. */
 typedef enum attn_page_layout {
   ATTN_PAGES_TOKEN_MAJOR = 0, /* page [page_size][Hkv][D]                  */
   ATTN_PAGES_HEAD_MAJOR = 1   /* page [Hkv][page_size][D]                  */
@@ -250,6 +251,28 @@ int attn_prefill(int dtype, const void *q, const void *k_cache,
                  const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
                  int max_length, int Lq, int prefix_len, float scale,
                  void *stream);
+
+/* Prefill against a paged prefix cache: the tutorial's prefix cache ("step14_3
+ * — batched attention: removing the per-head Python loop", problem section)
+ * keeps K and V token-major, [total_len, heads, d_head]; here the cache of
+ * sequence b is the list of pages block_table[b][.], as for
+ * attn_decode_paged. The result equals attn_prefill on the contiguous cache
+ * gathered from the pages (rows [0, prefix_len + Lq) of each sequence, which
+ * must already hold the new tokens' K and V).
+ *
+ *   k_pages, v_pages, block_table, page_layout, max_blocks, num_pages: as
+ *                for attn_decode_paged; rows past prefix_len + Lq are never
+ *                read (they may hold anything).
+ *   q, out, B, Hq, Hkv, Lq, prefix_len, scale: as for attn_prefill, with
+ *                max_length = max_blocks * page_size.
+ * Supported: ATTN_BF16, D == 64; page_size a multiple of 64 rows up to 65536;
+ * max_blocks * page_size < 2^31. ATTN_E_UNSUPPORTED for D == 128 or another
+ * page_size; ATTN_E_ARG as attn_decode_paged for the table arguments. */
+int attn_prefill_paged(int dtype, const void *q, const void *k_pages,
+                       const void *v_pages, const int32_t *block_table,
+                       int max_blocks, int page_size, int num_pages,
+                       int page_layout, void *out, int B, int Hq, int Hkv, int D,
+                       int Lq, int prefix_len, float scale, void *stream);
 
 /* --------------------------------------------------------------------------
  * Top-k sparse attention

@@ -11,7 +11,9 @@ from .attention import (  # noqa: F401
     decode_append_rope,
     decode_paged,
     decode_sequence,
+    gather_pages,
     prefill,
+    prefill_paged,
     rope_rotate,
     round_to_storage,
     topk_causal_select,

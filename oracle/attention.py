@@ -137,20 +137,15 @@ def decode_append(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
     return out, k2, v2
 
 
-def decode_paged(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray,
-                 block_table: np.ndarray,
-                 position_id: Optional[int] = None,
-                 seq_lens: Optional[np.ndarray] = None,
-                 scale: Optional[float] = None,
-                 layout: str = "token") -> np.ndarray:
-    """Decode over a paged cache: pages [num_pages, page_size, Hkv, D] hold
-    rows token-major (the head after the token, as the prefix cache of
-    [P2, problem section] stores K and V), or [num_pages, Hkv, page_size, D]
-    head-major; row r of sequence b is row r % page_size of page
-    block_table[b, r // page_size] (reading: the block-table indirection is
-    not spelled out on the pages). The logical cache is gathered row by row
-    and attended to as in ``decode``; page indices are clamped to the pages
-    that exist, as the library does.
+def gather_pages(k_pages: np.ndarray, v_pages: np.ndarray,
+                 block_table: np.ndarray, layout: str = "token"):
+    """The logical caches [B, Hkv, max_blocks * page_size, D] of a paged
+    cache: pages [num_pages, page_size, Hkv, D] hold rows token-major (the
+    head after the token, as the prefix cache of [P2, problem section]
+    stores K and V), or [num_pages, Hkv, page_size, D] head-major; row r of
+    sequence b is row r % page_size of page block_table[b, r // page_size]
+    (reading: the block-table indirection is not spelled out on the pages).
+    Page indices are clamped to the pages that exist, as the library does.
     """
     if layout == "token":
         num_pages, page_size, Hkv, D = k_pages.shape
@@ -170,6 +165,18 @@ def decode_paged(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray,
             else:
                 k[b, :, r, :] = k_pages[pg, :, r % page_size]
                 v[b, :, r, :] = v_pages[pg, :, r % page_size]
+    return k, v
+
+
+def decode_paged(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray,
+                 block_table: np.ndarray,
+                 position_id: Optional[int] = None,
+                 seq_lens: Optional[np.ndarray] = None,
+                 scale: Optional[float] = None,
+                 layout: str = "token") -> np.ndarray:
+    """Decode over a paged cache: the logical cache is gathered row by row
+    (``gather_pages``) and attended to as in ``decode``."""
+    k, v = gather_pages(k_pages, v_pages, block_table, layout)
     return decode(q, k, v, position_id=position_id, seq_lens=seq_lens,
                   scale=scale)
 
@@ -270,6 +277,17 @@ def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
             s = np.where(masked, -np.inf, s)
             out[b, h] = _softmax(s) @ V
     return out
+
+
+def prefill_paged(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray,
+                  block_table: np.ndarray, prefix_len: int,
+                  scale: Optional[float] = None,
+                  layout: str = "token") -> np.ndarray:
+    """Prefill whose cache is paged (the prefix cache of [P2, problem
+    section] keeps K and V per token): the logical cache is gathered
+    (``gather_pages``) and ``prefill`` runs on it."""
+    k, v = gather_pages(k_pages, v_pages, block_table, layout)
+    return prefill(q, k, v, prefix_len, scale)
 
 
 # ----------------------------------------------------------------------------

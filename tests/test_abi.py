@@ -274,6 +274,45 @@ def test_prefill_empty_is_a_noop():
     assert prefill(B=0) == OK
 
 
+def prefill_paged(**kw):
+    a = dict(dtype=BF16, q=P, k=P, v=P, table=P, max_blocks=64, page_size=64,
+             num_pages=64, layout=0, out=P, B=1, Hq=16, Hkv=16, D=64, Lq=1024,
+             prefix_len=3072, scale=0.125, stream=None)
+    a.update(kw)
+    return lib.attn_prefill_paged(
+        a["dtype"], a["q"], a["k"], a["v"], a["table"], a["max_blocks"],
+        a["page_size"], a["num_pages"], a["layout"], a["out"], a["B"], a["Hq"],
+        a["Hkv"], a["D"], a["Lq"], a["prefix_len"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=128), E_UNSUP),
+    (dict(page_size=32, max_blocks=128), E_UNSUP),   # not a multiple of 64
+    (dict(page_size=96), E_UNSUP),
+    (dict(page_size=0), E_ARG),
+    (dict(max_blocks=0), E_ARG),
+    (dict(num_pages=0), E_ARG),
+    (dict(layout=2), E_ARG),
+    (dict(layout=-1), E_ARG),
+    (dict(max_blocks=1 << 20, page_size=4096), E_ARG),  # 2^32 rows
+    (dict(max_blocks=63), E_ARG),      # prefix + Lq > max_blocks * page_size
+    (dict(table=None), E_ARG),
+    (dict(table=P + 2), E_ARG),
+    (dict(dtype=F32), E_UNSUP),
+    (dict(Hq=16, Hkv=3), E_ARG),
+    (dict(scale=0.0), E_ARG),
+    (dict(k=None), E_ARG),
+])
+def test_prefill_paged_rejects(kw, status):
+    assert prefill_paged(**kw) == status
+    assert lib.attn_last_error().decode().startswith("attn_prefill_paged")
+
+
+def test_prefill_paged_empty_is_a_noop():
+    assert prefill_paged(Lq=0, table=None) == OK
+    assert prefill_paged(B=0, table=None) == OK
+
+
 # ----------------------------------------------------------------------------
 # topk
 # ----------------------------------------------------------------------------

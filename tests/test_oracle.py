@@ -443,6 +443,38 @@ def test_prefill_matches_torch_sdpa_bottom_right_mask(B, Hq, Hkv, D, Lq,
     np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("layout", ["token", "head"])
+def test_prefill_paged_equals_contiguous_and_sdpa(layout):
+    # a prefix cache cut into shuffled pages (spare pages and rows past the
+    # new tokens hold NaN): the paged prefill sees exactly the contiguous rows
+    rng = np.random.default_rng(95)
+    B, Hq, Hkv, D, ps, Lq, prefix = 2, 4, 2, 8, 8, 11, 13
+    M = 32
+    q = rng.standard_normal((B, Hq, Lq, D)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, M, D)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, M, D)).astype(np.float32)
+    k[:, :, prefix + Lq:] = np.nan
+    v[:, :, prefix + Lq:] = np.nan
+    kp, vp, table = synth.paginate(k, v, ps, seed=95, dtype="f32",
+                                   layout=layout)
+    out = oracle.prefill_paged(q, kp, vp, table, prefix, layout=layout)
+    np.testing.assert_array_equal(out, oracle.prefill(q, k, v, prefix))
+    T = prefix + Lq
+    ref = F.scaled_dot_product_attention(
+        _t(q), _t(k[:, :, :T]), _t(v[:, :, :T]),
+        attn_mask=_bottom_right_mask(Lq, prefix), enable_gqa=True).numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    # swapping two blocks' table entries swaps those rows of the cache
+    t2 = table.copy()
+    t2[1, [0, 1]] = t2[1, [1, 0]]
+    k2, v2 = k.copy(), v.copy()
+    k2[1, :, 0:8], k2[1, :, 8:16] = k[1, :, 8:16], k[1, :, 0:8]
+    v2[1, :, 0:8], v2[1, :, 8:16] = v[1, :, 8:16], v[1, :, 0:8]
+    np.testing.assert_array_equal(
+        oracle.prefill_paged(q, kp, vp, t2, prefix, layout=layout),
+        oracle.prefill(q, k2, v2, prefix))
+
+
 def test_prefill_prefix0_equals_is_causal():
     # The going-further section's SDPA call with is_causal=True is exact
     # when there is no prefix.

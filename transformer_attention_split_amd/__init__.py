@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     attn_decode_paged,
     attn_decode_workspace_bytes,
     attn_prefill,
+    attn_prefill_paged,
     attn_topk,
     attn_topk_causal,
     lib,
@@ -27,5 +28,5 @@ from ._binding import (  # noqa: F401
 
 __all__ = ["attn_decode", "attn_decode_append", "attn_decode_append_rope",
            "attn_decode_paged",
-           "attn_prefill", "attn_topk", "attn_topk_causal",
+           "attn_prefill", "attn_prefill_paged", "attn_topk", "attn_topk_causal",
            "attn_decode_workspace_bytes", "AttnError", "AttnArgError"]

@@ -58,6 +58,9 @@ lib.attn_decode_paged.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _i,
 lib.attn_prefill.restype = _i
 lib.attn_prefill.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
                              _f, _p]
+lib.attn_prefill_paged.restype = _i
+lib.attn_prefill_paged.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _p, _i,
+                                   _i, _i, _i, _i, _i, _f, _p]
 lib.attn_topk.restype = _i
 lib.attn_topk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 lib.attn_topk_causal.restype = _i
@@ -66,7 +69,8 @@ lib.attn_topk_causal.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 EXPORTED = ("attn_status_str", "attn_last_error", "attn_abi_version",
             "attn_decode_workspace_bytes", "attn_decode", "attn_decode_append",
             "attn_decode_append_rope",
-            "attn_decode_paged", "attn_prefill", "attn_topk",
+            "attn_decode_paged", "attn_prefill", "attn_prefill_paged",
+            "attn_topk",
             "attn_topk_causal")
 
 
@@ -350,6 +354,54 @@ def attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                           Lq, int(prefix_len), float(scale),
                           _stream_handle(stream))
     _check(st, "attn_prefill")
+    return out
+
+
+def attn_prefill_paged(q: torch.Tensor, k_pages: torch.Tensor,
+                       v_pages: torch.Tensor, block_table: torch.Tensor, *,
+                       prefix_len: int, layout: str = "token",
+                       scale: Optional[float] = None,
+                       out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Causal prefill over a paged cache. q [B,Hq,Lq,D] bf16; pages
+    [num_pages,page_size,Hkv,D] (layout="token") or [num_pages,Hkv,page_size,D]
+    (layout="head"); block_table int32 [B,max_blocks] on the GPU. Returns out
+    [B,Hq,Lq,D]."""
+    _need_dense("q", q, 4)
+    _need_dense("k_pages", k_pages, 4)
+    _need_dense("v_pages", v_pages, 4)
+    _need_dense("block_table", block_table, 2)
+    if k_pages.shape != v_pages.shape:
+        raise ValueError("k_pages and v_pages shapes differ")
+    if not (q.dtype == k_pages.dtype == v_pages.dtype):
+        raise ValueError("q, k_pages and v_pages must share one dtype")
+    if block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32")
+    B, Hq, Lq, D = q.shape
+    if layout == "token":
+        num_pages, page_size, Hkv, Dk = k_pages.shape
+        code = ATTN_PAGES_TOKEN_MAJOR
+    elif layout == "head":
+        num_pages, Hkv, page_size, Dk = k_pages.shape
+        code = ATTN_PAGES_HEAD_MAJOR
+    else:
+        raise ValueError("layout must be 'token' or 'head'")
+    if Dk != D or block_table.shape[0] != B:
+        raise ValueError("page, block-table and query shapes do not match")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_dense("out", out, 4)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q's shape and dtype")
+    st = lib.attn_prefill_paged(
+        _dtype_code(q), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+        _ptr(block_table), block_table.shape[1], page_size, num_pages, code,
+        _ptr(out), B, Hq, Hkv, D, Lq, int(prefix_len), float(scale),
+        _stream_handle(stream))
+    _check(st, "attn_prefill_paged")
     return out
 
 

@@ -352,44 +352,102 @@ int attn_decode_paged(int dtype, const void *q, const void *k_pages,
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the prefill entry points; a.B == 0 on return: nothing to
+// launch.
+int prefill_check(const char *fn, int dtype, const void *q, const void *k,
+                  const void *v, void *out, int B, int Hq, int Hkv, int D,
+                  int max_length, int Lq, int prefix_len, float scale,
+                  attn::PrefillArgs &a) {
+  a = attn::PrefillArgs{};
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_E_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (dtype != ATTN_BF16)
+    return fail(ATTN_E_UNSUPPORTED, "%s: only ATTN_BF16 is supported", fn);
+  if (B < 0 || B > 65535)
+    return fail(ATTN_E_ARG, "%s: B=%d outside [0, 65535]", fn, B);
+  if (Hq < 1 || Hq > 65535 || Hkv < 1)
+    return fail(ATTN_E_ARG, "%s: Hq=%d Hkv=%d must be >= 1 (Hq <= 65535)", fn, Hq, Hkv);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_E_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (D < 1) return fail(ATTN_E_ARG, "%s: D=%d", fn, D);
+  if (D != 64 && D != 128)
+    return fail(ATTN_E_UNSUPPORTED, "%s: D=%d not in {64,128}", fn, D);
+  if (max_length < 1 || Lq < 0 || prefix_len < 0)
+    return fail(ATTN_E_ARG, "%s: max_length=%d Lq=%d prefix_len=%d", fn,
+                max_length, Lq, prefix_len);
+  if ((long long)prefix_len + Lq > max_length)
+    return fail(ATTN_E_ARG, "%s: prefix_len+Lq=%lld exceeds max_length=%d", fn,
+                (long long)prefix_len + Lq, max_length);
+  if (!fits({(double)B, (double)Hkv, (double)max_length, (double)D, 2.0}) ||
+      !fits({(double)B, (double)Hq, (double)max_length, (double)D, 2.0}))
+    return fail(ATTN_E_ARG, "%s: extents overflow", fn);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_E_ARG, "%s: scale must be finite and > 0", fn);
+  if (B == 0 || Lq == 0) return ok();  // nothing is read or written
+  if (!q || !k || !v || !out)
+    return fail(ATTN_E_ARG, "%s: null data pointer", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(ATTN_E_ARG, "%s: data pointers must be 16-byte aligned", fn);
+  a = attn::PrefillArgs{q, k, v, out, B, Hq, Hkv, D, max_length, Lq, prefix_len, scale};
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 int attn_prefill(int dtype, const void *q, const void *k_cache,
                  const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
                  int max_length, int Lq, int prefix_len, float scale,
                  void *stream) {
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
-    return fail(ATTN_E_ARG, "attn_prefill: unknown dtype %d", dtype);
-  if (dtype != ATTN_BF16)
-    return fail(ATTN_E_UNSUPPORTED, "attn_prefill: only ATTN_BF16 is supported");
-  if (B < 0 || B > 65535)
-    return fail(ATTN_E_ARG, "attn_prefill: B=%d outside [0, 65535]", B);
-  if (Hq < 1 || Hq > 65535 || Hkv < 1)
-    return fail(ATTN_E_ARG, "attn_prefill: Hq=%d Hkv=%d must be >= 1 (Hq <= 65535)", Hq, Hkv);
-  if (Hq % Hkv != 0)
-    return fail(ATTN_E_ARG, "attn_prefill: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-  if (D < 1) return fail(ATTN_E_ARG, "attn_prefill: D=%d", D);
-  if (D != 64 && D != 128)
-    return fail(ATTN_E_UNSUPPORTED, "attn_prefill: D=%d not in {64,128}", D);
-  if (max_length < 1 || Lq < 0 || prefix_len < 0)
-    return fail(ATTN_E_ARG, "attn_prefill: max_length=%d Lq=%d prefix_len=%d",
-                max_length, Lq, prefix_len);
-  if ((long long)prefix_len + Lq > max_length)
-    return fail(ATTN_E_ARG, "attn_prefill: prefix_len+Lq=%lld exceeds max_length=%d",
-                (long long)prefix_len + Lq, max_length);
-  if (!fits({(double)B, (double)Hkv, (double)max_length, (double)D, 2.0}) ||
-      !fits({(double)B, (double)Hq, (double)max_length, (double)D, 2.0}))
-    return fail(ATTN_E_ARG, "attn_prefill: extents overflow");
-  if (!std::isfinite(scale) || !(scale > 0.f))
-    return fail(ATTN_E_ARG, "attn_prefill: scale must be finite and > 0");
-  if (B == 0 || Lq == 0) return ok();  // nothing is read or written
-  if (!q || !k_cache || !v_cache || !out)
-    return fail(ATTN_E_ARG, "attn_prefill: null data pointer");
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(out, 16))
-    return fail(ATTN_E_ARG, "attn_prefill: data pointers must be 16-byte aligned");
-  attn::PrefillArgs a{q, k_cache, v_cache, out, B, Hq, Hkv, D, max_length,
-                      Lq, prefix_len, scale};
+  attn::PrefillArgs a;
+  const int st = prefill_check("attn_prefill", dtype, q, k_cache, v_cache, out,
+                               B, Hq, Hkv, D, max_length, Lq, prefix_len, scale, a);
+  if (st != ATTN_OK || a.B == 0) return st;
   hipError_t e = attn::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "attn_prefill launch");
+  return ok();
+}
+
+int attn_prefill_paged(int dtype, const void *q, const void *k_pages,
+                       const void *v_pages, const int32_t *block_table,
+                       int max_blocks, int page_size, int num_pages,
+                       int page_layout, void *out, int B, int Hq, int Hkv, int D,
+                       int Lq, int prefix_len, float scale, void *stream) {
+  const char *fn = "attn_prefill_paged";
+  if (D == 128)
+    return fail(ATTN_E_UNSUPPORTED, "%s: D=128 pages are not supported (D=64 only)", fn);
+  if (page_size < 1 || max_blocks < 1 || num_pages < 1)
+    return fail(ATTN_E_ARG, "%s: page_size=%d max_blocks=%d num_pages=%d must be >= 1",
+                fn, page_size, max_blocks, num_pages);
+  if (page_size % 64 != 0 || page_size > 65536)
+    return fail(ATTN_E_UNSUPPORTED,
+                "%s: page_size=%d must be a multiple of 64 rows and <= 65536", fn, page_size);
+  if (page_layout != ATTN_PAGES_TOKEN_MAJOR && page_layout != ATTN_PAGES_HEAD_MAJOR)
+    return fail(ATTN_E_ARG, "%s: page_layout=%d", fn, page_layout);
+  if ((long long)max_blocks * page_size > 0x7fffffffLL)
+    return fail(ATTN_E_ARG, "%s: max_blocks*page_size exceeds 2^31-1", fn);
+  if (Hkv >= 1 && D >= 1 &&
+      !fits({(double)num_pages, (double)page_size, (double)Hkv, (double)D, 2.0}))
+    return fail(ATTN_E_ARG, "%s: page pool extents overflow", fn);
+  attn::PrefillArgs a;
+  const int st = prefill_check(fn, dtype, q, k_pages, v_pages, out, B, Hq, Hkv,
+                               D, max_blocks * page_size, Lq, prefix_len, scale, a);
+  if (st != ATTN_OK || a.B == 0) return st;
+  if (!block_table) return fail(ATTN_E_ARG, "%s: null block_table", fn);
+  if (!aligned(block_table, 4))
+    return fail(ATTN_E_ARG, "%s: block_table must be 4-byte aligned", fn);
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  a.head_major = page_layout == ATTN_PAGES_HEAD_MAJOR;
+  hipError_t e = attn::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
 }
 

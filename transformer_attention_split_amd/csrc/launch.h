@@ -54,6 +54,11 @@ struct PrefillArgs {
   void *out;
   int B, Hq, Hkv, D, max_length, Lq, prefix_len;
   float scale;
+  // Paged caches (null: contiguous): as for DecodeArgs; max_length =
+  // max_blocks * page_size and page_size is a multiple of the 64-row tile.
+  const int32_t *block_table = nullptr;
+  int max_blocks = 0, page_size = 0, num_pages = 0;
+  int head_major = 0;
 };
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);

@@ -421,11 +421,17 @@ __device__ __forceinline__ float quad_max(float m) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// PAGED: K and V rows come from pages of page_size rows (a multiple of the
+// 64-row tile, so a tile never straddles pages) named by
+// block_table[b][row / page_size] (clamped to the pages that exist); pages
+// are token-major [page][row][Hkv][D] or head-major [page][Hkv][row][D].
+template <bool PAGED>
 __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
     const uint16_t *__restrict__ qg, const uint16_t *__restrict__ kg,
     const uint16_t *__restrict__ vg, uint16_t *__restrict__ outg, int NH,
     int Hq, int Hkv, int max_length, int Lq, int prefix, float qk_scale,
-    int n_qtiles, int heads_per_xcd) {
+    int n_qtiles, int heads_per_xcd, const int32_t *__restrict__ block_table,
+    int max_blocks, int page_size, int num_pages, int head_major) {
   using T = P64;
   constexpr int D = T::D, KS = T::KS, NDB = T::NDB, NKB = T::NKB;
   constexpr int NB = T::NB, NQW = T::NQW, BM = T::BM, ROWB = T::ROWB;
@@ -464,11 +470,14 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
   const bool g_active = qg0 < Lq;
   const int g_kmax = prefix + min(qg0 + NQW - 1, Lq - 1);  // last visible key
 
-  const size_t kvbase = ((size_t)b * Hkv + kvh) * (size_t)max_length * D;
+  const size_t kvbase = PAGED ? 0 : ((size_t)b * Hkv + kvh) * (size_t)max_length * D;
   // wave (0, kq) streams K, wave (1, kq) streams V
+  const uint16_t *kvsrc = qgi == 0 ? kg : vg;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t *>((qgi == 0 ? kg : vg) + kvbase), (short)0, kv_len * ROWB,
-      kBufferFlags);
+      const_cast<uint16_t *>(kvsrc + kvbase), (short)0, kv_len * ROWB, kBufferFlags);
+  // bytes between consecutive rows of one kv head (paged token-major pages
+  // interleave the heads)
+  const int prs = PAGED && !head_major ? Hkv * ROWB : ROWB;
 
   // This wave's queries as B operands (column li of block nb), multiplied
   // by scale * log2 e and rounded back to bf16, so the products give scores
@@ -513,16 +522,56 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
     const int pos = l % 8;
     const int chunk = qgi == 0 ? pos ^ ((4 * par + lg) & 7)  // K: c ^ ((r >> 1) & 7)
                                : pos ^ (2 * lg);            // V: c ^ 2((r >> 1) & 3)
-    dma_off[par] = (l / 8) * ROWB + chunk * 16;
+    dma_off[par] = (l / 8) * prs + chunk * 16;
+  }
+  // Paged: element offset of the first row of tile t (rows r0 .. r0+63 of
+  // this kv head) in the page pool.
+  auto tile_offset = [&](int t) -> uint64_t {
+    const int r0 = t * BN;
+    const int bi = min(r0 / page_size, max_blocks - 1);
+    const int pg = min(max(block_table[(size_t)b * max_blocks + bi], 0), num_pages - 1);
+    const int rin = r0 % page_size;
+    return head_major ? (((uint64_t)pg * Hkv + kvh) * page_size + rin) * D
+                      : ((uint64_t)pg * page_size + rin) * Hkv * D + (uint64_t)kvh * D;
+  };
+  // Lane i holds (in two halves) the offset of this wave's tile of
+  // iteration i: one lookup per lane here, none before the issues.
+  uint32_t po_lo = 0, po_hi = 0;
+  if constexpr (PAGED) {
+    const uint64_t off = tile_offset(l * NKQ + kq);
+    po_lo = (uint32_t)off;
+    po_hi = (uint32_t)(off >> 32);
   }
   auto issue = [&](int it, unsigned char *kbuf, unsigned char *vbuf) {
     unsigned char *dst = (qgi == 0 ? kbuf : vbuf) + kq * T::T_BYTES;
     const int t = it * NKQ + kq;
+    if constexpr (PAGED) {
+      // the tile's rows in the pool (lane `it` of po_lo/po_hi for the first
+      // 64 iterations, else looked up: b, kq and it are wave-uniform) and a
+      // resource over the rows that exist: rows past kv_len read as zeros
+      uint64_t off;
+      if (it < 64)
+        off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)po_hi, it) << 32) |
+              (uint32_t)__builtin_amdgcn_readlane((int)po_lo, it);
+      else
+        off = tile_offset(t);
+      // (readfirstlane: the resource must sit in scalar registers; a clamp
+      // computed on the vector ALUs would otherwise turn every load into a
+      // loop over distinct resource values)
+      const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(BN, kv_len - t * BN)) * prs);
+      const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(kvsrc + off), (short)0, nbytes, kBufferFlags);
 #pragma unroll
-    for (int jj = 0; jj < T::DMA; ++jj)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void_t *)(dst + jj * 1024), 16, dma_off[jj & 1],
-          t * T::T_BYTES + jj * 1024, 0, 0);
+      for (int jj = 0; jj < T::DMA; ++jj)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rt, (lds_void_t *)(dst + jj * 1024), 16, dma_off[jj & 1], jj * 8 * prs, 0, 0);
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < T::DMA; ++jj)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (lds_void_t *)(dst + jj * 1024), 16, dma_off[jj & 1],
+            t * T::T_BYTES + jj * 1024, 0, 0);
+    }
   };
   // A-operand reads of K: block kb, k-step ks -> row 16 kb + li, chunk
   // 4 ks + lg at position (4 ks + lg) ^ (li >> 1).
@@ -712,6 +761,7 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
   }
 }
 
+template <bool PAGED>
 hipError_t launch_64(const PrefillArgs &a, hipStream_t stream) {
   using T = P64;
   const int n_qtiles = (a.Lq + T::BM - 1) / T::BM;
@@ -719,11 +769,12 @@ hipError_t launch_64(const PrefillArgs &a, hipStream_t stream) {
   const int heads_per_xcd = (NH + kXcds - 1) / kXcds;
   const long blocks = (long)kXcds * heads_per_xcd * n_qtiles;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  prefill64_kernel<<<dim3((unsigned)blocks), T::THREADS, 0, stream>>>(
+  prefill64_kernel<PAGED><<<dim3((unsigned)blocks), T::THREADS, 0, stream>>>(
       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
       static_cast<const uint16_t *>(a.v), static_cast<uint16_t *>(a.out), NH,
       a.Hq, a.Hkv, a.max_length, a.Lq, a.prefix_len, a.scale * kLog2e,
-      n_qtiles, heads_per_xcd);
+      n_qtiles, heads_per_xcd, a.block_table, a.max_blocks, a.page_size,
+      a.num_pages, a.head_major);
   return hipGetLastError();
 }
 
@@ -752,7 +803,9 @@ hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
-  return a.D == 64 ? launch_64(a, stream) : launch_d<128>(a, stream);
+  if (a.block_table != nullptr)  // paged caches: D = 64 only (checked by the caller)
+    return launch_64<true>(a, stream);
+  return a.D == 64 ? launch_64<false>(a, stream) : launch_d<128>(a, stream);
 }
 
 }  // namespace attn
