@@ -265,9 +265,10 @@ int attn_prefill(int dtype, const void *q, const void *k_cache,
  *                read (they may hold anything).
  *   q, out, B, Hq, Hkv, Lq, prefix_len, scale: as for attn_prefill, with
  *                max_length = max_blocks * page_size.
- * Supported: ATTN_BF16, D == 64; page_size a multiple of 64 rows up to 65536;
- * max_blocks * page_size < 2^31. ATTN_E_UNSUPPORTED for D == 128 or another
- * page_size; ATTN_E_ARG as attn_decode_paged for the table arguments. */
+ * Supported: ATTN_BF16, D in {64, 128}; page_size a multiple of the kernel's
+ * key tile, 4096 / D rows (64 at D = 64, 32 at D = 128), up to 65536;
+ * max_blocks * page_size < 2^31. ATTN_E_UNSUPPORTED for another page_size;
+ * ATTN_E_ARG as attn_decode_paged for the table arguments. */
 int attn_prefill_paged(int dtype, const void *q, const void *k_pages,
                        const void *v_pages, const int32_t *block_table,
                        int max_blocks, int page_size, int num_pages,

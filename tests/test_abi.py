@@ -286,8 +286,9 @@ def prefill_paged(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(D=128), E_UNSUP),
-    (dict(page_size=32, max_blocks=128), E_UNSUP),   # not a multiple of 64
+    (dict(D=128, page_size=48, max_blocks=100), E_UNSUP),  # not a multiple of 32
+    (dict(D=96), E_UNSUP),
+    (dict(page_size=32, max_blocks=128), E_UNSUP),   # D=64: not a multiple of 64
     (dict(page_size=96), E_UNSUP),
     (dict(page_size=0), E_ARG),
     (dict(max_blocks=0), E_ARG),

@@ -63,6 +63,7 @@ def test_prefill_paged_prefix3072(layout, page_size):
     check_paged(inp, page_size, layout, 81, with_oracle=page_size == 64)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("layout", ["token", "head"])
 @pytest.mark.parametrize("B,Hq,Hkv,Lq,prefix,extra,ps", [
     (1, 2, 2, 1, 0, 0, 64),        # single token, no prefix
@@ -70,12 +71,15 @@ def test_prefill_paged_prefix3072(layout, page_size):
     (2, 4, 2, 100, 0, 9, 128),     # pure causal, ragged query tile, GQA
     (1, 3, 3, 64, 64, 0, 64),      # tile-aligned
     (1, 8, 2, 65, 63, 30, 192),    # one past a tile
+    (1, 4, 4, 33, 31, 3, 96),      # D=128 tiles: 32-row page multiples
     (2, 2, 2, 200, 333, 17, 64),   # ragged everything, several sequences
 ])
-def test_prefill_paged_shapes(layout, B, Hq, Hkv, Lq, prefix, extra, ps):
-    inp = synth.prefill(2000 + Lq + prefix, B, Hq, Hkv, 64, Lq, prefix,
+def test_prefill_paged_shapes(D, layout, B, Hq, Hkv, Lq, prefix, extra, ps):
+    if ps % (4096 // D):
+        pytest.skip("page size not a multiple of the D=64 tile (64 rows)")
+    inp = synth.prefill(2000 + Lq + prefix, B, Hq, Hkv, D, Lq, prefix,
                         max_length=prefix + Lq + extra, dtype="bf16")
-    say(f"prefill_paged B={B} Hq={Hq} Hkv={Hkv} Lq={Lq} prefix={prefix} "
+    say(f"prefill_paged D={D} B={B} Hq={Hq} Hkv={Hkv} Lq={Lq} prefix={prefix} "
         f"page={ps} {layout}")
     check_paged(inp, ps, layout, 82 + Lq)
 
@@ -94,3 +98,11 @@ def test_prefill_paged_clamped_and_shared_pages():
         return t
     say("prefill_paged clamped and shared pages")
     check_paged(inp, 64, "token", 84, table_fix=fix, extra_pages=0)
+
+
+@pytest.mark.parametrize("layout", ["token", "head"])
+def test_prefill_paged_d128_long(layout):
+    inp = synth.prefill(85, 1, 8, 2, 128, 300, 1000, max_length=1400,
+                        dtype="bf16")
+    say(f"prefill_paged D=128 Hq=8 Hkv=2 Lq=300 prefix=1000 page=32 {layout}")
+    check_paged(inp, 32, layout, 86)

@@ -419,14 +419,14 @@ int attn_prefill_paged(int dtype, const void *q, const void *k_pages,
                        int page_layout, void *out, int B, int Hq, int Hkv, int D,
                        int Lq, int prefix_len, float scale, void *stream) {
   const char *fn = "attn_prefill_paged";
-  if (D == 128)
-    return fail(ATTN_E_UNSUPPORTED, "%s: D=128 pages are not supported (D=64 only)", fn);
   if (page_size < 1 || max_blocks < 1 || num_pages < 1)
     return fail(ATTN_E_ARG, "%s: page_size=%d max_blocks=%d num_pages=%d must be >= 1",
                 fn, page_size, max_blocks, num_pages);
-  if (page_size % 64 != 0 || page_size > 65536)
+  const int tile = D == 128 ? 32 : 64;  // keys per kernel tile (8 KiB of K)
+  if (page_size % tile != 0 || page_size > 65536)
     return fail(ATTN_E_UNSUPPORTED,
-                "%s: page_size=%d must be a multiple of 64 rows and <= 65536", fn, page_size);
+                "%s: page_size=%d must be a multiple of %d rows and <= 65536", fn,
+                page_size, tile);
   if (page_layout != ATTN_PAGES_TOKEN_MAJOR && page_layout != ATTN_PAGES_HEAD_MAJOR)
     return fail(ATTN_E_ARG, "%s: page_layout=%d", fn, page_layout);
   if ((long long)max_blocks * page_size > 0x7fffffffLL)

@@ -7,33 +7,31 @@
 // score matrix never reaches HBM. New token i sits at cache row prefix+i and
 // sees rows [0, prefix+i].
 //
-// One workgroup = 8 waves = 2 query groups of one head, walking the 64-key
-// tiles up to the causal bound of its last query:
-//   * Waves: query group qg = w / 4 x key quarter kq = w % 4 (tiles t with
-//     t % 4 == kq). A wave holds NB 16-query column blocks (2 at D = 64: every
-//     K and V operand feeds two MFMAs, halving operand traffic per FLOP; 1 at
-//     D = 128, for the register budget). Two waves per SIMD hide each other's
-//     latencies and overlap one's matrix work with the other's softmax. The
-//     four key quarters of a query group are merged (log-sum-exp) in LDS at
-//     the end.
+// One kernel for D = 64 and D = 128 (prefill_lds_kernel): one workgroup =
+// 8 waves = 64 queries of one head, walking the key tiles (8 KiB of K each:
+// 64 keys at D = 64, 32 at D = 128) up to the causal bound of its last query.
+//   * Waves: query group qg = w / 4 (32 queries, two 16-column blocks: every
+//     K and V operand feeds two products) x key quarter kq = w % 4 (tiles t
+//     with t % 4 == kq). Two waves per SIMD. The four key quarters of a query
+//     group are merged (log-sum-exp) in LDS at the end.
 //   * Block -> work map: workgroup id i runs on XCD i % 8; every query tile of
 //     one head goes to the same XCD, so the head's K and V are fetched from
 //     HBM once into that XCD's L2; on each XCD tiles run longest first.
-//   * K is read straight from L1/L2 into the A operand of
-//     v_mfma_f32_16x16x32_bf16 (16 key rows x 32 dims per instruction). V is
-//     copied row-major into LDS for all four tiles of an iteration
-//     (double-buffered) and read back with the transposing LDS read
-//     ds_read_b64_tr_b16, which delivers the d-major A operand of the P·V
-//     product directly; the next iteration's V (and, for D = 64, K) loads are
+//   * Each iteration's four K tiles and four V tiles cross the L1 path once
+//     per workgroup, as buffer loads that write LDS directly, double-buffered,
+//     one workgroup barrier per iteration; the next iteration's loads are
 //     issued before the current one is computed.
-//   * Sᵀ = K·Qᵀ puts each lane on one query and 4 keys of every 16-key block:
-//     the operand layout of Oᵀ += Vᵀ·Pᵀ, so P never leaves registers.
-//   * Softmax in the exp2 domain: the running max is kept on raw scores
-//     (scale > 0 commutes with max), p = exp2(fma(s, scale*log2 e, -m)); the
-//     output is rescaled only when the running max grows by more than 8 (log2
-//     units), so p stays below 2^8 and most tiles skip the rescale. Row sums
-//     come from the matrix cores: an all-ones A operand times Pᵀ sums the same
-//     bf16 probabilities the output uses.
+//   * Sᵀ = K·Qᵀ on v_mfma_f32_16x16x32_bf16 (A = 16 key rows from LDS, B =
+//     the wave's queries in registers) puts each lane on one query and 4 keys
+//     of every 16-key block: the operand layout of Oᵀ += Vᵀ·Pᵀ, so P never
+//     leaves registers; the Vᵀ operand comes from transposing LDS reads
+//     (ds_read_b64_tr_b16).
+//   * Softmax in the exp2 domain with the scale folded into the queries and
+//     the running max into the accumulator start (each probability is one
+//     v_exp_f32); the output is rescaled only when the running max grows by
+//     more than 8 (log2 units). Row sums come from the matrix cores: an
+//     all-ones A operand times Pᵀ sums the same bf16 probabilities the output
+//     uses.
 //   * Only tiles that cross the diagonal evaluate the mask; tiles past a
 //     query group's last visible key are skipped.
 #include "common.h"
@@ -47,10 +45,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BN = 64;   // keys per tile
 constexpr int NKQ = 4;   // key quarters (waves per query group)
 constexpr int NQG = 2;   // query groups per workgroup
-constexpr int kThreads = 512;
 constexpr int kXcds = 8;
 constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag
 // buffer resource word 3 for raw (untyped, stride 0) 32-bit accesses
@@ -79,339 +75,52 @@ __device__ __forceinline__ u32x2_t read_tr16(const uint16_t *lds) {
   return __builtin_bit_cast(u32x2_t, r);
 }
 
-template <int D>
-struct Tile {
-  static constexpr int NB = D <= 64 ? 2 : 1;  // 16-query column blocks per wave
-  static constexpr int NQW = 16 * NB;         // queries per wave
-  static constexpr int BM = NQG * NQW;        // queries per workgroup
-  static constexpr int KS = D / 32;    // MFMA k-steps of K·Qᵀ
-  static constexpr int NDB = D / 16;   // 16-wide output blocks
-  static constexpr int NKB = BN / 16;  // 16-key blocks per tile
-  static constexpr int SV = D + 16;    // V row stride in LDS (elements): the
-                                       // 4 rows of one transposing read start
-                                       // 8 banks apart
-  static constexpr int VT = BN * SV;   // elements of one V tile
-  static constexpr bool PREFETCH_K = D <= 64;              // register budget
-  static constexpr int LDS_V = 2 * NKQ * VT * 2;           // bytes, 2 buffers
-  static constexpr int LDS_MERGE = (NQG * NKQ * NQW * D + 2 * NQG * NKQ * NQW) * 4;
-  static constexpr int LDS = LDS_V > LDS_MERGE ? LDS_V : LDS_MERGE;
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(
-    const uint16_t *__restrict__ qg, const uint16_t *__restrict__ kg,
-    const uint16_t *__restrict__ vg, uint16_t *__restrict__ outg, int NH,
-    int Hq, int Hkv, int max_length, int Lq, int prefix, float qk_scale,
-    int n_qtiles, int heads_per_xcd) {
-  using T = Tile<D>;
-  constexpr int KS = T::KS, NDB = T::NDB, NKB = T::NKB, SV = T::SV;
-  constexpr int NB = T::NB, NQW = T::NQW, BM = T::BM;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t *Vt = reinterpret_cast<uint16_t *>(smem);  // [2][NKQ][BN][SV]
-
-  // ---- work item: (head instance, query tile) -----------------------------------
-  const int id = blockIdx.x;
-  const int xcd = id % kXcds;
-  const int k = id / kXcds;
-  const int j = xcd + kXcds * (k % heads_per_xcd);  // head instance b*Hq + h
-  if (j >= NH) return;
-  const int qt = n_qtiles - 1 - k / heads_per_xcd;  // longest tiles first
-  const int b = j / Hq;
-  const int h = j % Hq;
-  const int kvh = h / (Hq / Hkv);
-
-  const int tid = threadIdx.x;
-  const int w = tid / 64;
-  const int l = tid % 64;
-  const int li = l % 16;
-  const int lg = l / 16;
-  const int kq = w % NKQ;   // key quarter
-  const int qgi = w / NKQ;  // query group
-
-  const int kv_len = prefix + Lq;
-  const int q_end = min((qt + 1) * BM, Lq);
-  const int n_tiles = (prefix + q_end + BN - 1) / BN;
-  const int n_iter = (n_tiles + NKQ - 1) / NKQ;
-  const int qg0 = qt * BM + qgi * NQW;  // first query of this wave's group
-  const bool g_active = qg0 < Lq;
-  const int g_kmax = prefix + min(qg0 + NQW - 1, Lq - 1);  // last visible key
-
-  const size_t kvbase = ((size_t)b * Hkv + kvh) * (size_t)max_length * D;
-  const uint16_t *kbase = kg + kvbase;
-  const uint16_t *vbase = vg + kvbase;
-
-  // This wave's queries as B operands (column li of block nb).
-  bf16x8_t qf[NB][KS];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int qme = qg0 + nb * 16 + li;
-    const size_t qrow = ((size_t)j * Lq + (size_t)qme) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (qme < Lq) v = *reinterpret_cast<const u32x4_t *>(qg + qrow + ks * 32 + 8 * lg);
-      qf[nb][ks] = as_bf16x8(v);
-    }
-  }
-  // byte addresses of lanes l ^ 16 and l ^ 32 for ds_bpermute
-  const int bp16 = (l ^ 16) * 4;
-  const int bp32 = (l ^ 32) * 4;
-  const u32x4_t ones_w = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-  const bf16x8_t ones = as_bf16x8(ones_w);
-
-  f32x4_t o[NB][NDB];
-  f32x4_t lacc[NB];
-  float mc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) o[nb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    lacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    mc[nb] = kNegInf;
-  }
-
-  // K rows (A operands) and V rows are loaded from clamped row indices:
-  // rows at or past kv_len only occur in tiles that cross the diagonal,
-  // where every real query masks them (p = 0), so any finite cache row will
-  // do and no load needs a guard; rows past kv_len are never read.
-  const u32x4_t *k4 = reinterpret_cast<const u32x4_t *>(kbase);
-  const u32x4_t *v4 = reinterpret_cast<const u32x4_t *>(vbase);
-  const unsigned last_row = (unsigned)(kv_len - 1);
-
-  auto load_k = [&](int t, u32x4_t (&dst)[NKB][KS]) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const unsigned row = min((unsigned)(t * BN + kb * 16 + li), last_row);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) dst[kb][ks] = k4[row * (D / 8) + ks * 4 + lg];
-    }
-  };
-  // V of the NKQ tiles of one iteration, copied row-major into LDS: item =
-  // (tile, row, 8-dim chunk), chunks fastest, so one load instruction covers
-  // whole rows and one 16-byte LDS write per item.
-  constexpr int VITEMS = NKQ * BN * (D / 8);
-  constexpr int VCH = VITEMS / kThreads;   // items per thread
-  static_assert(VITEMS % kThreads == 0, "V items per thread");
-  u32x4_t vreg[VCH];
-  auto load_v = [&](int it) {
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + i * kThreads;
-      const int col = c % (D / 8);
-      const int row = (c / (D / 8)) % BN;
-      const int tl = c / (BN * (D / 8));
-      const unsigned r = (unsigned)((it * NKQ + tl) * BN + row);
-      vreg[i] = v4[min(r, last_row) * (D / 8) + col];
-    }
-  };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + i * kThreads;
-      const int col = c % (D / 8);
-      const int row = (c / (D / 8)) % BN;
-      const int tl = c / (BN * (D / 8));
-      *reinterpret_cast<u32x4_t *>(Vt + (size_t)(buf * NKQ + tl) * T::VT +
-                                   row * SV + col * 8) = vreg[i];
-    }
-  };
-
-  // One iteration: this wave's tile of iteration `it` with K operands `kc`;
-  // the next iteration's V (and, for D = 64, K into `kx`) is prefetched.
-  auto step = [&](int it, u32x4_t (&kc)[NKB][KS], u32x4_t (&kx)[NKB][KS]) {
-    // Loads and the LDS store run unconditionally (row indices are clamped,
-    // so the extra loads of the last iteration stay in bounds): with no
-    // branch around them the compiler's wait counts cover exactly the
-    // previous iteration's loads and the prefetch overlaps this iteration.
-    const int buf = it & 1;
-    const int t = it * NKQ + kq;
-    const int tn = t + NKQ;
-    load_v(it + 1);
-    if constexpr (T::PREFETCH_K) load_k(tn, kx);
-    const int j0 = t * BN;
-    if (t < n_tiles && g_active && j0 <= g_kmax) {
-      const uint16_t *vt = Vt + (size_t)(buf * NKQ + kq) * T::VT;
-      // ---- Sᵀ = K·Qᵀ (raw scores), every K operand feeds NB query blocks ----
-      f32x4_t s[NB][NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[nb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8_t a = as_bf16x8(kc[kb][ks]);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            s[nb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[nb][ks], s[nb][kb], 0, 0, 0);
-        }
-      }
-      const bool diag = j0 + BN - 1 > prefix + qg0;
-      bf16x8_t pb[NB][BN / 32];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        // ---- causal mask (diagonal tiles only) -----------------------------------
-        if (diag) [[unlikely]] {
-          // key j0 + 16 kb + 4 lg + r is visible iff 16 kb + r <= lim
-          const int lim = prefix + qg0 + nb * 16 + li - j0 - 4 * lg;
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (16 * kb + r > lim) s[nb][kb][r] = kNegInf;
-        }
-        // ---- running max over the 4 lanes of the query; lazy rescale ---------
-        float m0 = max3(s[nb][0][0], s[nb][0][1], s[nb][0][2]);
-        m0 = max3(m0, s[nb][0][3], s[nb][1][0]);
-#pragma unroll
-        for (int kb = 1; kb < NKB; ++kb) {
-          m0 = max3(m0, s[nb][kb][1], s[nb][kb][2]);
-          m0 = kb + 1 < NKB ? max3(m0, s[nb][kb][3], s[nb][kb + 1][0])
-                            : fmaxf(m0, s[nb][kb][3]);
-        }
-        m0 = fmaxf(m0, __int_as_float(__builtin_amdgcn_ds_bpermute(bp16, __float_as_int(m0))));
-        m0 = fmaxf(m0, __int_as_float(__builtin_amdgcn_ds_bpermute(bp32, __float_as_int(m0))));
-        const float mloc_c = m0 * qk_scale;
-        if (__any(mloc_c > mc[nb] + kRescaleSlack)) [[unlikely]] {
-          const float mnew = fmaxf(mc[nb], mloc_c);
-          // a query with no visible key yet keeps max -inf: no rescale (and
-          // no -inf - -inf)
-          const float alpha = mnew == mc[nb] ? 1.f : fast_exp2(mc[nb] - mnew);
-          mc[nb] = mnew;
-          lacc[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) o[nb][db] *= alpha;
-        }
-        // every score of a query with max -inf is masked: any finite offset
-        // gives p = 0 (and -mc would be +inf)
-        const float nmc = mc[nb] == kNegInf ? 0.f : -mc[nb];
-#pragma unroll
-        for (int t2 = 0; t2 < BN / 32; ++t2) {
-          float p[8];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p[r] = fast_exp2(fmaf(s[nb][2 * t2][r], qk_scale, nmc));
-            p[4 + r] = fast_exp2(fmaf(s[nb][2 * t2 + 1][r], qk_scale, nmc));
-          }
-          const u32x4_t pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                              pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-          pb[nb][t2] = as_bf16x8(pw);
-        }
-      }
-      // ---- row sums and Oᵀ += Vᵀ·Pᵀ, every V operand feeds NB query blocks ---
-#pragma unroll
-      for (int t2 = 0; t2 < BN / 32; ++t2) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          lacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[nb][t2], lacc[nb], 0, 0, 0);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          // transposing reads: lane li of lane group lg receives
-          // V[key][16 db + li] for keys 32 t2 + 4 lg + 0..3 and + 16
-          const uint16_t *src = vt + (32 * t2 + 4 * lg + li / 4) * SV + db * 16 + 4 * (li % 4);
-          const u32x2_t lo = read_tr16(src);
-          const u32x2_t hi = read_tr16(src + 16 * SV);
-          const u32x4_t av = {lo[0], lo[1], hi[0], hi[1]};
-          const bf16x8_t a = as_bf16x8(av);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            o[nb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[nb][t2], o[nb][db], 0, 0, 0);
-        }
-      }
-    }
-    store_v(buf ^ 1);
-    if constexpr (!T::PREFETCH_K) load_k(tn, kx);
-    __syncthreads();
-  };
-
-  u32x4_t kfa[NKB][KS];
-  load_v(0);
-  load_k(kq, kfa);
-  store_v(0);
-  __syncthreads();
-  if constexpr (T::PREFETCH_K) {
-    // two register sets alternate roles (no copies)
-    u32x4_t kfb[NKB][KS];
-    for (int it = 0; it < n_iter; it += 2) {
-      step(it, kfa, kfb);
-      if (it + 1 < n_iter) step(it + 1, kfb, kfa);
-    }
-  } else {
-    // the next tile's K is loaded into the same registers after use
-    for (int it = 0; it < n_iter; ++it) step(it, kfa, kfa);
-  }
-
-  // ---- merge the key quarters of each query group (log-sum-exp), store -----------
-  float *mo = reinterpret_cast<float *>(smem);         // [NQG][NKQ][NQW][D]
-  float *mm = mo + NQG * NKQ * NQW * D;                // [NQG][NKQ][NQW]
-  float *ml = mm + NQG * NKQ * NQW;                    // [NQG][NKQ][NQW]
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int qi = nb * 16 + li;  // query inside the group
-    float *dst = mo + ((size_t)(qgi * NKQ + kq) * NQW + qi) * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<f32x4_t *>(dst + db * 16 + 4 * lg) = o[nb][db];
-    if (lg == 0) {
-      mm[(qgi * NKQ + kq) * NQW + qi] = mc[nb];
-      ml[(qgi * NKQ + kq) * NQW + qi] = lacc[nb][0];
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < BM * D / 2; i += kThreads) {
-    const int q = (2 * i) / D;       // query inside the workgroup
-    const int d = (2 * i) % D;       // even dimension; this thread does d, d+1
-    const int grp = q / NQW, qi = q % NQW;
-    const int qglob = qt * BM + q;
-    if (qglob >= Lq) continue;
-    float M = kNegInf;
-#pragma unroll
-    for (int kk = 0; kk < NKQ; ++kk) M = fmaxf(M, mm[(grp * NKQ + kk) * NQW + qi]);
-    float a0 = 0.f, a1 = 0.f, lt = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < NKQ; ++kk) {
-      const float wgt = fast_exp2(mm[(grp * NKQ + kk) * NQW + qi] - M);
-      const float *src = mo + ((size_t)(grp * NKQ + kk) * NQW + qi) * D + d;
-      a0 = fmaf(wgt, src[0], a0);
-      a1 = fmaf(wgt, src[1], a1);
-      lt = fmaf(wgt, ml[(grp * NKQ + kk) * NQW + qi], lt);
-    }
-    const float inv = 1.f / lt;
-    *reinterpret_cast<uint32_t *>(outg + ((size_t)j * Lq + qglob) * D + d) =
-        pack_bf16x2(a0 * inv, a1 * inv);
-  }
-}
-
 // ---------------------------------------------------------------------------
-// D = 64: K and V staged once per workgroup in LDS
+// K and V staged once per workgroup in LDS
 // ---------------------------------------------------------------------------
-// A workgroup of 8 waves takes 64 queries: query group qg = w / 4 (32
-// queries, 2 column blocks of 16) x key quarter kq = w % 4 (tiles t with
-// t % 4 == kq). Two waves per SIMD hide each other's latencies.
-//   * Every 64-key tile of K and of V crosses the L1 path once per
-//     workgroup: iteration it's four K tiles and four V tiles are loaded with
-//     buffer loads that write LDS directly (wave (0, kq) loads K tile kq,
-//     wave (1, kq) loads V tile kq), double-buffered, one workgroup barrier
-//     per iteration. The next iteration's loads are issued before this
-//     iteration is computed.
-//   * LDS tiles are 64 rows of 128 bytes, unpadded, with the 16-byte chunk c
-//     of row r at position c ^ ((r >> 1) & 7) for K (the 16 rows x 16 bytes
-//     of one A-operand read fall on distinct banks) and c ^ 2*((r >> 1) & 3)
-//     for V (likewise for the 16 rows x 32 bytes of one transposing read).
+//   * LDS tiles are unpadded rows of 2 D bytes; the 16-byte chunk c of row r
+//     sits at c ^ swz_k(r) for K (the 16 rows x 16 bytes of one A-operand
+//     read fall on distinct banks) and c ^ swz_v(r) for V (the 16 rows x 32
+//     bytes of one transposing read spread evenly over the banks).
 //   * K and V are read through buffer resources limited to the rows
 //     [0, prefix + Lq): rows past the end read as zeros.
 //   * The running max is reduced across the four lanes of a query with
 //     v_permlane16_swap / v_permlane32_swap.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-struct P64 {
-  static constexpr int D = 64, NB = 2, NQW = 16 * NB, BM = NQG * NQW;
+// One 16-byte-per-lane direct-to-LDS buffer load (1 KiB per wave at dst).
+// (A plain function: called with template-dependent arguments straight from
+// a kernel template, the builtin made the host pass drop the kernel's launch
+// stub without a diagnostic.)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *dst,
+                                      int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, soff, 0, 0);
+}
+
+template <int D_>
+struct PT {
+  static constexpr int D = D_, NB = 2, NQW = 16 * NB, BM = NQG * NQW;
   static constexpr int THREADS = 64 * NQG * NKQ;
+  static constexpr int BN = 4096 / D;            // keys per tile: 8 KiB of K
   static constexpr int KS = D / 32, NDB = D / 16, NKB = BN / 16;
   static constexpr int ROWB = D * 2;             // bytes per cache row
+  static constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
+  static constexpr int RPL = 1024 / ROWB;        // rows per 1 KiB LDS load
   static constexpr int T_BYTES = BN * ROWB;      // one tile: 8 KiB
   static constexpr int DMA = T_BYTES / 1024;     // 1 KiB LDS loads per tile
   static constexpr int BUF = NKQ * T_BYTES;      // one iteration of K (or V)
+  static constexpr int NPAR = D == 64 ? 2 : 4;   // distinct swizzles per load
+  // LDS position of 16-byte chunk c of tile row r. K: the 16 rows x 16
+  // bytes of one A-operand read fall on distinct banks; V: the 16 rows x 32
+  // bytes of one transposing read spread evenly over the banks.
+  static __device__ __forceinline__ int swz_k(int r) {
+    return D == 64 ? (r >> 1) & 7 : r & 15;
+  }
+  static __device__ __forceinline__ int swz_v(int r) {
+    return D == 64 ? 2 * ((r >> 1) & 3) : 2 * (r & 7);
+  }
 };
+using P64 = PT<64>;
 
 __device__ __forceinline__ float quad_max(float m) {
   // max over lanes l, l ^ 16, l ^ 32, l ^ 48
@@ -422,24 +131,25 @@ __device__ __forceinline__ float quad_max(float m) {
 }
 
 // PAGED: K and V rows come from pages of page_size rows (a multiple of the
-// 64-row tile, so a tile never straddles pages) named by
+// tile, so a tile never straddles pages) named by
 // block_table[b][row / page_size] (clamped to the pages that exist); pages
 // are token-major [page][row][Hkv][D] or head-major [page][Hkv][row][D].
-template <bool PAGED>
-__global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
+template <int D_, bool PAGED>
+__global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
     const uint16_t *__restrict__ qg, const uint16_t *__restrict__ kg,
     const uint16_t *__restrict__ vg, uint16_t *__restrict__ outg, int NH,
     int Hq, int Hkv, int max_length, int Lq, int prefix, float qk_scale,
     int n_qtiles, int heads_per_xcd, const int32_t *__restrict__ block_table,
     int max_blocks, int page_size, int num_pages, int head_major) {
-  using T = P64;
-  constexpr int D = T::D, KS = T::KS, NDB = T::NDB, NKB = T::NKB;
+  using T = PT<D_>;
+  constexpr int D = T::D, KS = T::KS, NDB = T::NDB, NKB = T::NKB, BN = T::BN;
   constexpr int NB = T::NB, NQW = T::NQW, BM = T::BM, ROWB = T::ROWB;
   // K and V buffers of the two iterations in flight, as separate LDS
   // objects: the compiler then tells a direct load into one from reads of
   // another and does not make the reads wait for it.
   __shared__ __attribute__((aligned(16))) unsigned char kb0[T::BUF], kb1[T::BUF],
       vb0[T::BUF], vb1[T::BUF];
+  __shared__ float mml[2 * NQG * NQW * NKQ];  // merge: running max and sum
 
   // ---- work item: (head instance, query tile) -----------------------------------
   const int id = blockIdx.x;
@@ -514,17 +224,17 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
   }
 
   // Loads: load jj of a tile fills LDS bytes [1024 jj, 1024 jj + 1024); lane
-  // l writes position l % 8 of row 8 jj + l / 8 and reads the chunk that
-  // belongs there.
-  int dma_off[2];
+  // l writes position l % CPR of row RPL jj + l / CPR and reads the chunk
+  // that belongs there (the swizzles repeat every RPL * NPAR rows).
+  int dma_off[T::NPAR];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int pos = l % 8;
-    const int chunk = qgi == 0 ? pos ^ ((4 * par + lg) & 7)  // K: c ^ ((r >> 1) & 7)
-                               : pos ^ (2 * lg);            // V: c ^ 2((r >> 1) & 3)
-    dma_off[par] = (l / 8) * prs + chunk * 16;
+  for (int par = 0; par < T::NPAR; ++par) {
+    const int pos = l % T::CPR;
+    const int r = T::RPL * par + l / T::CPR;
+    const int chunk = pos ^ (qgi == 0 ? T::swz_k(r) : T::swz_v(r));
+    dma_off[par] = (l / T::CPR) * prs + chunk * 16;
   }
-  // Paged: element offset of the first row of tile t (rows r0 .. r0+63 of
+  // Paged: element offset of the first row of tile t (rows r0 .. r0+BN-1 of
   // this kv head) in the page pool.
   auto tile_offset = [&](int t) -> uint64_t {
     const int r0 = t * BN;
@@ -563,27 +273,27 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
           const_cast<uint16_t *>(kvsrc + off), (short)0, nbytes, kBufferFlags);
 #pragma unroll
       for (int jj = 0; jj < T::DMA; ++jj)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rt, (lds_void_t *)(dst + jj * 1024), 16, dma_off[jj & 1], jj * 8 * prs, 0, 0);
+        dma16(rt, dst + jj * 1024, dma_off[jj % T::NPAR], jj * T::RPL * prs);
     } else {
 #pragma unroll
       for (int jj = 0; jj < T::DMA; ++jj)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (lds_void_t *)(dst + jj * 1024), 16, dma_off[jj & 1],
-            t * T::T_BYTES + jj * 1024, 0, 0);
+        dma16(rs, dst + jj * 1024, dma_off[jj % T::NPAR], t * T::T_BYTES + jj * 1024);
     }
   };
   // A-operand reads of K: block kb, k-step ks -> row 16 kb + li, chunk
-  // 4 ks + lg at position (4 ks + lg) ^ (li >> 1).
+  // 4 ks + lg at position (4 ks + lg) ^ swz_k(li) (swz_k has period 16).
   int kro[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kro[ks] = li * ROWB + (((4 * ks + lg) ^ (li >> 1)) * 16);
-  // Transposing reads of V: lane (li, lg) names row 4 lg + li / 4 (+ 32 t2,
-  // + 16) and the 8 bytes of chunk 2 db + (li >> 1) % 2, half li % 2.
+  for (int ks = 0; ks < KS; ++ks) kro[ks] = li * ROWB + (((4 * ks + lg) ^ T::swz_k(li)) * 16);
+  // Transposing reads of V: lane (li, lg) names row r = 4 lg + li / 4 (+ 32
+  // t2, + 16: swz_v has period 8) and the 8 bytes of chunk 2 db + (li >> 1)
+  // % 2, half li % 2; swz_v is even, so the chunk pair 2 db, 2 db + 1 moves
+  // as a unit to position pair 2 (db ^ swz_v(r) / 2).
   int tro[NDB];
   {
-    const int fh = (2 * lg + (li >> 3)) & 3;
-    const int base = (4 * lg + (li >> 2)) * ROWB + ((li >> 1) & 1) * 16 + (li & 1) * 8;
+    const int r = 4 * lg + (li >> 2);
+    const int fh = T::swz_v(r) / 2;
+    const int base = r * ROWB + ((li >> 1) & 1) * 16 + (li & 1) * 8;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) tro[db] = base + 32 * (db ^ fh);
   }
@@ -714,8 +424,17 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
   //    c ^ (qi % 16), so the 16 rows of one write fall on distinct banks;
   // 3. every thread adds the four quarters of 4 consecutive outputs and stores
   //    them as bf16.
-  float *mm = reinterpret_cast<float *>(vb0);  // [NQG][NQW][NKQ]
-  float *ml = mm + NQG * NQW * NKQ;            // [NQG][NQW][NKQ]
+  float *mm = mml;                    // [NQG][NQW][NKQ]
+  float *ml = mm + NQG * NQW * NKQ;   // [NQG][NQW][NKQ]
+  // fp32 output of (group, quarter): D = 64 puts a group's four quarters in
+  // kb0 / kb1; D = 128 two per buffer, quarters 2 and 3 in vb0 / vb1
+  constexpr int QBYTES = NQW * D * 4;
+  constexpr int QPER = T::BUF / QBYTES;
+  static_assert(QPER * QBYTES == T::BUF && NKQ % QPER == 0, "merge layout");
+  auto quarter = [&](int grp, int kk) -> float * {
+    unsigned char *bb = kk / QPER == 0 ? (grp == 0 ? kb0 : kb1) : (grp == 0 ? vb0 : vb1);
+    return reinterpret_cast<float *>(bb + (kk % QPER) * QBYTES);
+  };
   if (lg == 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -726,7 +445,7 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
   }
   __syncthreads();
   {
-    float *mo = reinterpret_cast<float *>(qgi == 0 ? kb0 : kb1) + kq * NQW * D;
+    float *mo = quarter(qgi, kq);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int qi = nb * 16 + li;
@@ -752,24 +471,24 @@ __global__ __launch_bounds__(P64::THREADS) void prefill64_kernel(
     const int grp = q / NQW, qi = q % NQW;
     const int qglob = qt * BM + q;
     if (qglob >= Lq) continue;
-    const float *mo = reinterpret_cast<const float *>(grp == 0 ? kb0 : kb1) + qi * D + ((c ^ (qi % 16)) * 4);
-    f32x4_t acc = *reinterpret_cast<const f32x4_t *>(mo);
+    const int off = qi * D + ((c ^ (qi % 16)) * 4);
+    f32x4_t acc = *reinterpret_cast<const f32x4_t *>(quarter(grp, 0) + off);
 #pragma unroll
-    for (int kk = 1; kk < NKQ; ++kk) acc += *reinterpret_cast<const f32x4_t *>(mo + kk * NQW * D);
+    for (int kk = 1; kk < NKQ; ++kk) acc += *reinterpret_cast<const f32x4_t *>(quarter(grp, kk) + off);
     *reinterpret_cast<u32x2_t *>(outg + ((size_t)j * Lq + qglob) * D + 4 * c) =
         u32x2_t{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
   }
 }
 
-template <bool PAGED>
-hipError_t launch_64(const PrefillArgs &a, hipStream_t stream) {
-  using T = P64;
+template <int D, bool PAGED>
+hipError_t launch_lds(const PrefillArgs &a, hipStream_t stream) {
+  using T = PT<D>;
   const int n_qtiles = (a.Lq + T::BM - 1) / T::BM;
   const int NH = a.B * a.Hq;
   const int heads_per_xcd = (NH + kXcds - 1) / kXcds;
   const long blocks = (long)kXcds * heads_per_xcd * n_qtiles;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  prefill64_kernel<PAGED><<<dim3((unsigned)blocks), T::THREADS, 0, stream>>>(
+  prefill_lds_kernel<D, PAGED><<<dim3((unsigned)blocks), T::THREADS, 0, stream>>>(
       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
       static_cast<const uint16_t *>(a.v), static_cast<uint16_t *>(a.out), NH,
       a.Hq, a.Hkv, a.max_length, a.Lq, a.prefix_len, a.scale * kLog2e,
@@ -778,34 +497,12 @@ hipError_t launch_64(const PrefillArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
-  using T = Tile<D>;
-  const int n_qtiles = (a.Lq + T::BM - 1) / T::BM;
-  const int NH = a.B * a.Hq;
-  const int heads_per_xcd = (NH + kXcds - 1) / kXcds;
-  const long blocks = (long)kXcds * heads_per_xcd * n_qtiles;
-  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  if (T::LDS > 65536) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&prefill_kernel<D>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
-    if (e != hipSuccess) return e;
-  }
-  prefill_kernel<D><<<dim3((unsigned)blocks), kThreads, T::LDS, stream>>>(
-      static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
-      static_cast<const uint16_t *>(a.v), static_cast<uint16_t *>(a.out), NH,
-      a.Hq, a.Hkv, a.max_length, a.Lq, a.prefix_len, a.scale * kLog2e,
-      n_qtiles, heads_per_xcd);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
-  if (a.block_table != nullptr)  // paged caches: D = 64 only (checked by the caller)
-    return launch_64<true>(a, stream);
-  return a.D == 64 ? launch_64<false>(a, stream) : launch_d<128>(a, stream);
+  if (a.block_table != nullptr)
+    return a.D == 64 ? launch_lds<64, true>(a, stream) : launch_lds<128, true>(a, stream);
+  return a.D == 64 ? launch_lds<64, false>(a, stream) : launch_lds<128, false>(a, stream);
 }
 
 }  // namespace attn
