@@ -304,6 +304,41 @@ def bench_paged(torch, tas, dec, steps, page_size, layout):
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the decode workload
 # ----------------------------------------------------------------------------
+def bench_prefill_d128(torch, tas, synth, n=20):
+    """The prefill workload's shape at head size 128 (16 heads, prefix 3072 +
+    1024 new tokens), n back-to-back calls between two events."""
+    import numpy as np
+    p = synth.WORKLOADS["prefill_prefix3072"].params
+    inp = synth.prefill(p["seed"], 1, 16, 16, 128, p["Lq"], p["prefix_len"],
+                        p["max_length"], "bf16", poison=False,
+                        scale=128 ** -0.5)
+    q, k, v = (bf16_dev(x, torch) for x in (inp.q, inp.k_cache, inp.v_cache))
+    out = torch.empty_like(q)
+
+    def fn():
+        tas.attn_prefill(q, k, v, prefix_len=p["prefix_len"],
+                         scale=128 ** -0.5, out=out)
+    for _ in range(3):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    flops = 4 * 128 * 16 * sum(p["prefix_len"] + i + 1 for i in range(p["Lq"]))
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return dict(workload="prefill_prefix3072 at D=128 (16 heads)",
+                us_back_to_back=round(us, 2), flops=flops,
+                TFLOPs_back_to_back=round(flops / us / 1e6, 1),
+                frac_of_bf16_mfma_peak=round(flops / us / 1e6
+                                             / BF16_MFMA_PEAK_TFLOPS, 4))
+
+
 def bench_prefill_paged(torch, tas, pre, page_size, layout, n=20):
     """attn_prefill_paged on the prefill workload's cache cut into shuffled
     pages of `page_size` rows, against attn_prefill on the contiguous cache:
@@ -556,6 +591,9 @@ def main():
         secondary["decode_paged_ragged_b64"] = [
             bench_paged(torch, tas, dec, args.steps, ps, lay)
             for lay in ("token", "head") for ps in (64, 256)]
+        log("prefill at D=128 ...")
+        secondary["prefill_d128_prefix3072"] = bench_prefill_d128(torch, tas,
+                                                                  synth)
         log("paged prefill ...")
         secondary["prefill_paged_prefix3072"] = [
             bench_prefill_paged(torch, tas, pre, ps, lay)
