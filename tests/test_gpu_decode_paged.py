@@ -107,3 +107,23 @@ def test_paged_out_of_range_table_entries_are_clamped():
                               seq_lens=lens, scale=inp.scale)
     err = max_abs_err(out, ref)
     assert err <= tol("bf16"), err
+
+
+@pytest.mark.parametrize("layout", ["token", "head"])
+def test_paged_more_sequences_than_the_device_work_map(layout):
+    # more than 256 sequences: the grid's plain order instead of the
+    # on-device work map; still the contiguous decode bit for bit
+    rng = np.random.default_rng(65)
+    lens = rng.integers(0, 257, 300).astype(np.int32)
+    inp = synth.decode_ragged(65, B=300, Hq=4, Hkv=2, D=64, max_length=256,
+                              dtype="bf16", lengths=lens)
+    kp, vp, table = synth.paginate(inp.k_cache, inp.v_cache, 64, 65,
+                                   layout=layout)
+    say(f"decode_paged bf16 B=300 {layout}-major")
+    out = run_paged(inp, kp, vp, table, split_rows=64, layout=layout)
+    ref = tas.attn_decode(to_dev(inp.q, "bf16"), to_dev(inp.k_cache, "bf16"),
+                          to_dev(inp.v_cache, "bf16"),
+                          seq_lens=torch.from_numpy(lens).cuda(),
+                          scale=inp.scale, split_rows=64)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)

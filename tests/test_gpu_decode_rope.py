@@ -165,3 +165,14 @@ def test_rope_append_ragged_standard_tables():
     cos, sin = rope_tables(_rows(inp), 128)
     say("decode_append_rope bf16 ragged B=16 max=2048 standard tables")
     check_rope(inp, kn, vn, cos, sin)
+
+
+def test_rope_append_more_sequences_than_the_device_work_map():
+    rng = np.random.default_rng(76)
+    lens = rng.integers(0, 150, 300).astype(np.int32)
+    inp = synth.decode_ragged(76, B=300, Hq=4, Hkv=2, D=64, max_length=150,
+                              dtype="bf16", lengths=lens)
+    kn, vn = synth.new_token_kv(76, 300, 2, 64, "bf16")
+    cos, sin = rope_tables(_rows(inp), 64)
+    say("decode_append_rope bf16 ragged B=300 split_rows=32")
+    check_rope(inp, kn, vn, cos, sin, split_rows=32)

@@ -106,3 +106,14 @@ def test_prefill_paged_d128_long(layout):
                         dtype="bf16")
     say(f"prefill_paged D=128 Hq=8 Hkv=2 Lq=300 prefix=1000 page=32 {layout}")
     check_paged(inp, 32, layout, 86)
+
+
+@pytest.mark.parametrize("D,prefix,ps", [(64, 16500, 256), (128, 8300, 128)])
+def test_prefill_paged_past_the_lane_table(D, prefix, ps):
+    # a wave keeps the page offsets of its first 64 iterations in lanes;
+    # later tiles (past 64 iterations x 4 quarters x 4096/D rows) are looked
+    # up one by one
+    inp = synth.prefill(87 + D, 1, 2, 1, D, 100, prefix,
+                        max_length=prefix + 100 + 60, dtype="bf16")
+    say(f"prefill_paged D={D} prefix={prefix} Lq=100 page={ps} (lookup path)")
+    check_paged(inp, ps, "token", 88, with_oracle=True)
