@@ -304,20 +304,18 @@ def bench_paged(torch, tas, dec, steps, page_size, layout):
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the decode workload
 # ----------------------------------------------------------------------------
-def bench_prefill_d128(torch, tas, synth, n=20):
-    """The prefill workload's shape at head size 128 (16 heads, prefix 3072 +
-    1024 new tokens), n back-to-back calls between two events."""
-    import numpy as np
+def bench_prefill_shape(torch, tas, synth, D, H, n=20):
+    """The prefill workload's prefix and new tokens with head size D and H
+    heads, n back-to-back calls between two events."""
     p = synth.WORKLOADS["prefill_prefix3072"].params
-    inp = synth.prefill(p["seed"], 1, 16, 16, 128, p["Lq"], p["prefix_len"],
-                        p["max_length"], "bf16", poison=False,
-                        scale=128 ** -0.5)
+    inp = synth.prefill(p["seed"], 1, H, H, D, p["Lq"], p["prefix_len"],
+                        p["max_length"], "bf16", poison=False, scale=D ** -0.5)
     q, k, v = (bf16_dev(x, torch) for x in (inp.q, inp.k_cache, inp.v_cache))
     out = torch.empty_like(q)
 
     def fn():
-        tas.attn_prefill(q, k, v, prefix_len=p["prefix_len"],
-                         scale=128 ** -0.5, out=out)
+        tas.attn_prefill(q, k, v, prefix_len=p["prefix_len"], scale=D ** -0.5,
+                         out=out)
     for _ in range(3):
         fn()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -329,10 +327,10 @@ def bench_prefill_d128(torch, tas, synth, n=20):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / n
-    flops = 4 * 128 * 16 * sum(p["prefix_len"] + i + 1 for i in range(p["Lq"]))
+    flops = 4 * D * H * sum(p["prefix_len"] + i + 1 for i in range(p["Lq"]))
     del q, k, v, out
     torch.cuda.empty_cache()
-    return dict(workload="prefill_prefix3072 at D=128 (16 heads)",
+    return dict(workload=f"prefill_prefix3072 at D={D} ({H} heads)",
                 us_back_to_back=round(us, 2), flops=flops,
                 TFLOPs_back_to_back=round(flops / us / 1e6, 1),
                 frac_of_bf16_mfma_peak=round(flops / us / 1e6
@@ -591,9 +589,11 @@ def main():
         secondary["decode_paged_ragged_b64"] = [
             bench_paged(torch, tas, dec, args.steps, ps, lay)
             for lay in ("token", "head") for ps in (64, 256)]
-        log("prefill at D=128 ...")
-        secondary["prefill_d128_prefix3072"] = bench_prefill_d128(torch, tas,
-                                                                  synth)
+        log("prefill at D=128 and with 32 heads ...")
+        secondary["prefill_d128_prefix3072"] = bench_prefill_shape(
+            torch, tas, synth, 128, 16)
+        secondary["prefill_h32_prefix3072"] = bench_prefill_shape(
+            torch, tas, synth, 64, 32)
         log("paged prefill ...")
         secondary["prefill_paged_prefix3072"] = [
             bench_prefill_paged(torch, tas, pre, ps, lay)
