@@ -99,14 +99,16 @@ def test_prefill_repeatable_and_prefix0_causal():
     assert torch.equal(a[:, :, 0], v0)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("B,Hq,Hkv,Lq,prefix", [
-    (1, 64, 8, 512, 100),    # 512 workgroups: two per CU, 32-key tiles
+    (1, 64, 8, 512, 100),    # 512 workgroups: two per CU
     (2, 32, 32, 520, 77),    # 576 workgroups, ragged last query tile
 ])
-def test_prefill_grids_with_two_workgroups_per_cu(B, Hq, Hkv, Lq, prefix):
-    inp = synth.prefill(3000 + Lq, B, Hq, Hkv, 64, Lq, prefix,
+def test_prefill_grids_with_two_workgroups_per_cu(D, B, Hq, Hkv, Lq, prefix):
+    # D = 64: 4 KiB tiles; D = 128: two key parts per query group
+    inp = synth.prefill(3000 + Lq + D, B, Hq, Hkv, D, Lq, prefix,
                         max_length=prefix + Lq + 40, dtype="bf16")
-    say(f"prefill D=64 B={B} Hq={Hq} Hkv={Hkv} Lq={Lq} prefix={prefix} "
-        "(4 KiB tiles)")
+    say(f"prefill D={D} B={B} Hq={Hq} Hkv={Hkv} Lq={Lq} prefix={prefix} "
+        "(two workgroups per CU)")
     err = max_abs_err(to_host64(run(inp)), oracle_of(inp))
     assert err <= tol("bf16"), err

@@ -119,10 +119,11 @@ def test_prefill_paged_past_the_lane_table(D, prefix, ps):
     check_paged(inp, ps, "token", 88, with_oracle=True)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("layout", ["token", "head"])
-def test_prefill_paged_two_workgroups_per_cu(layout):
-    # 512 workgroups: the 4 KiB-tile kernel reads the pages
-    inp = synth.prefill(89, 1, 64, 8, 64, 512, 100, max_length=640,
+def test_prefill_paged_two_workgroups_per_cu(D, layout):
+    # 512 workgroups: the half-LDS kernels read the pages
+    inp = synth.prefill(89 + D, 1, 64, 8, D, 512, 100, max_length=640,
                         dtype="bf16")
-    say(f"prefill_paged D=64 Hq=64 Hkv=8 Lq=512 prefix=100 page=64 {layout}")
+    say(f"prefill_paged D={D} Hq=64 Hkv=8 Lq=512 prefix=100 page=64 {layout}")
     check_paged(inp, 64, layout, 90)

@@ -45,7 +45,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int NKQ = 4;   // key quarters (waves per query group)
 constexpr int NQG = 2;   // query groups per workgroup
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;  // compute units of an MI355X
@@ -98,12 +97,15 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, soff, 0, 0);
 }
 
-// BN_: keys per tile. 4096 / D makes 8 KiB tiles (one workgroup per CU:
-// 130 KiB of LDS); 32 at D = 64 makes 4 KiB tiles (66 KiB: two workgroups
-// per CU, used when the grid has enough workgroups to fill both slots).
-template <int D_, int BN_ = 4096 / D_>
+// BN_: keys per tile. 4096 / D makes 8 KiB tiles; with NKQ_ = 4 key parts
+// (waves per query group) one workgroup takes 130 KiB of LDS, one per CU.
+// For grids with at least two workgroups per CU, 4 KiB tiles at D = 64, or
+// two key parts at D = 128, halve that, so that two workgroups share a CU
+// out of step with each other.
+template <int D_, int BN_ = 4096 / D_, int NKQ_ = 4>
 struct PT {
   static constexpr int D = D_, NB = 2, NQW = 16 * NB, BM = NQG * NQW;
+  static constexpr int NKQ = NKQ_;
   static constexpr int THREADS = 64 * NQG * NKQ;
   static constexpr int BN = BN_;
   static constexpr int KS = D / 32, NDB = D / 16, NKB = BN / 16;
@@ -139,14 +141,15 @@ __device__ __forceinline__ float quad_max(float m) {
 // tile, so a tile never straddles pages) named by
 // block_table[b][row / page_size] (clamped to the pages that exist); pages
 // are token-major [page][row][Hkv][D] or head-major [page][Hkv][row][D].
-template <int D_, bool PAGED, int BN_>
+template <int D_, bool PAGED, int BN_, int NKQ_>
 __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
     const uint16_t *__restrict__ qg, const uint16_t *__restrict__ kg,
     const uint16_t *__restrict__ vg, uint16_t *__restrict__ outg, int NH,
     int Hq, int Hkv, int max_length, int Lq, int prefix, float qk_scale,
     int n_qtiles, int heads_per_xcd, const int32_t *__restrict__ block_table,
     int max_blocks, int page_size, int num_pages, int head_major) {
-  using T = PT<D_, BN_>;
+  using T = PT<D_, BN_, NKQ_>;
+  constexpr int NKQ = T::NKQ;
   constexpr int D = T::D, KS = T::KS, NDB = T::NDB, NKB = T::NKB, BN = T::BN;
   constexpr int NB = T::NB, NQW = T::NQW, BM = T::BM, ROWB = T::ROWB;
   // K and V buffers of the two iterations in flight, as separate LDS
@@ -454,13 +457,19 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int qi = nb * 16 + li;
-      const f32x4_t m4 = *reinterpret_cast<const f32x4_t *>(&mm[(qgi * NQW + qi) * NKQ]);
-      const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(&ml[(qgi * NQW + qi) * NKQ]);
-      const float M = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      float m4[NKQ], l4[NKQ];
+#pragma unroll
+      for (int kk = 0; kk < NKQ; ++kk) {
+        m4[kk] = mm[(qgi * NQW + qi) * NKQ + kk];
+        l4[kk] = ml[(qgi * NQW + qi) * NKQ + kk];
+      }
+      float M = m4[0];
+#pragma unroll
+      for (int kk = 1; kk < NKQ; ++kk) M = fmaxf(M, m4[kk]);
       float L = 0.f;
 #pragma unroll
       for (int kk = 0; kk < NKQ; ++kk)
-        // a key quarter that saw no key of this query contributes nothing
+        // a key part that saw no key of this query contributes nothing
         L = fmaf(m4[kk] == kNegInf ? 0.f : fast_exp2(m4[kk] - M), l4[kk], L);
       // (a query past the end of the sequence has L = 0; it is not stored)
       const float wgt = mc[nb] == kNegInf ? 0.f : fast_exp2(mc[nb] - M) / L;
@@ -485,15 +494,15 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
   }
 }
 
-template <int D, bool PAGED, int BN = 4096 / D>
+template <int D, bool PAGED, int BN = 4096 / D, int NKQ = 4>
 hipError_t launch_lds(const PrefillArgs &a, hipStream_t stream) {
-  using T = PT<D, BN>;
+  using T = PT<D, BN, NKQ>;
   const int n_qtiles = (a.Lq + T::BM - 1) / T::BM;
   const int NH = a.B * a.Hq;
   const int heads_per_xcd = (NH + kXcds - 1) / kXcds;
   const long blocks = (long)kXcds * heads_per_xcd * n_qtiles;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  prefill_lds_kernel<D, PAGED, BN><<<dim3((unsigned)blocks), T::THREADS, 0, stream>>>(
+  prefill_lds_kernel<D, PAGED, BN, NKQ><<<dim3((unsigned)blocks), T::THREADS, 0, stream>>>(
       static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
       static_cast<const uint16_t *>(a.v), static_cast<uint16_t *>(a.out), NH,
       a.Hq, a.Hkv, a.max_length, a.Lq, a.prefix_len, a.scale * kLog2e,
@@ -506,15 +515,20 @@ hipError_t launch_lds(const PrefillArgs &a, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   const bool paged = a.block_table != nullptr;
-  if (a.D == 128)
-    return paged ? launch_lds<128, true>(a, stream) : launch_lds<128, false>(a, stream);
-  // D = 64: with at least two workgroups per CU to run, 4 KiB tiles let two
-  // of them share a CU out of step with each other (measured: 32 heads of the
-  // prefill workload 43.6 us against 49.4 us with 8 KiB tiles); with fewer,
-  // 8 KiB tiles halve the iterations (16 heads: 26.8 us against 28.4 us).
+  // With at least two workgroups per CU to run, the half-LDS forms let two
+  // of them share a CU out of step with each other (measured at D = 64: 32
+  // heads of the prefill workload 43.6 us with 4 KiB tiles against 49.4 us);
+  // with fewer, the full form halves the iterations (16 heads: 26.8 us
+  // against 28.4 us).
   const long blocks = (long)kXcds * ((a.B * a.Hq + kXcds - 1) / kXcds) *
                       ((a.Lq + P64::BM - 1) / P64::BM);
-  if (blocks >= 2L * kCUs)
+  const bool two_per_cu = blocks >= 2L * kCUs;
+  if (a.D == 128) {
+    if (two_per_cu)
+      return paged ? launch_lds<128, true, 32, 2>(a, stream) : launch_lds<128, false, 32, 2>(a, stream);
+    return paged ? launch_lds<128, true>(a, stream) : launch_lds<128, false>(a, stream);
+  }
+  if (two_per_cu)
     return paged ? launch_lds<64, true, 32>(a, stream) : launch_lds<64, false, 32>(a, stream);
   return paged ? launch_lds<64, true>(a, stream) : launch_lds<64, false>(a, stream);
 }
