@@ -17,6 +17,12 @@ top-k figures are reported beside it. Inputs are synthetic (seeded N(0,1),
 bf16 rounded to nearest even), generated once and resident in HBM before the
 timed region starts.
 
+Unless --no-secondary is given, the `secondary` object also times the fused
+append (plain and with the rotary embedding) and the paged decode on the
+decode batch, the decoder-causal top-k, the paged prefill, the prefill shape
+at head size 128 and with 32 heads, and the single-sequence decode at
+position 8000 (cold and warm, from a captured graph).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
