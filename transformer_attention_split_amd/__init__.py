@@ -1,6 +1,9 @@
-"""MI355X (gfx950) KV-cache attention: split-KV decode, causal prefill
-against a cached prefix, and top-k sparse scores, as hand-written HIP kernels
-behind a C ABI (``include/attn.h``). This package is the thin Python binding.
+"""MI355X (gfx950) KV-cache attention: split-KV decode (plain, with the
+current token's cache append, with the rotary embedding in that append, or
+over a paged cache), causal prefill against a cached prefix (contiguous or
+paged), and top-k sparse scores (encoder and decoder-causal forms), as
+hand-written HIP kernels behind a C ABI (``include/attn.h``). This package is
+the thin Python binding.
 """
 from ._binding import (  # noqa: F401
     ATTN_BF16,
