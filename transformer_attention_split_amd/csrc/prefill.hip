@@ -26,10 +26,10 @@
 //     of every 16-key block: the operand layout of Oᵀ += Vᵀ·Pᵀ, so P never
 //     leaves registers; the Vᵀ operand comes from transposing LDS reads
 //     (ds_read_b64_tr_b16).
-//   * Softmax in the exp2 domain with the scale folded into the queries and
-//     the running max into the accumulator start (each probability is one
-//     v_exp_f32); the output is rescaled only when the running max grows by
-//     more than 8 (log2 units). Row sums come from the matrix cores: an
+//   * Softmax in the exp2 domain: each probability is one fma (fp32 score
+//     times scale·log2 e, minus the running max) and one v_exp_f32; the
+//     output is rescaled only when the running max grows by more than 8
+//     (log2 units). Row sums come from the matrix cores: an
 //     all-ones A operand times Pᵀ sums the same bf16 probabilities the output
 //     uses.
 //   * Only tiles that cross the diagonal evaluate the mask; tiles past a
@@ -197,9 +197,10 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
   // interleave the heads)
   const int prs = PAGED && !head_major ? Hkv * ROWB : ROWB;
 
-  // This wave's queries as B operands (column li of block nb), multiplied
-  // by scale * log2 e and rounded back to bf16, so the products give scores
-  // in log2 units directly.
+  // This wave's queries as B operands (column li of block nb), as stored:
+  // the scale is applied to the fp32 scores (folding it into bf16 queries
+  // would add a relative error of 2^-9 to every score, which large scores
+  // turn into visible weight errors).
   bf16x8_t qf[NB][KS];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -209,9 +210,6 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t v = {0u, 0u, 0u, 0u};
       if (qme < Lq) v = *reinterpret_cast<const u32x4_t *>(qg + qrow + ks * 32 + 8 * lg);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        v[e] = pack_bf16x2(bf16lo(v[e]) * qk_scale, bf16hi(v[e]) * qk_scale);
       qf[nb][ks] = as_bf16x8(v);
     }
   }
@@ -220,15 +218,13 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
 
   f32x4_t o[NB][NDB];
   f32x4_t lacc[NB];
-  float mc[NB];       // running max (log2 units), -inf before the first key
-  f32x4_t sinit[NB];  // score accumulators start at -mc (0 while mc = -inf)
+  float mc[NB];  // running max (log2 units), -inf before the first key
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
     for (int i = 0; i < NDB; ++i) o[nb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     lacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     mc[nb] = kNegInf;
-    sinit[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   // Loads: load jj of a tile fills LDS bytes [1024 jj, 1024 jj + 1024); lane
@@ -318,7 +314,7 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) s[nb][kb] = sinit[nb];
+      for (int nb = 0; nb < NB; ++nb) s[nb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8_t a = as_bf16x8(*reinterpret_cast<const u32x4_t *>(kt + kb * 16 * ROWB + kro[ks]));
@@ -341,9 +337,9 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
           for (int r = 0; r < 4; ++r)
             if (16 * kb + r > lim) s[nb][kb][r] = kNegInf;
       }
-      // ---- lazy rescale: the scores are already relative to the running max
-      // (to 0 before the first visible key); only a tile whose scores exceed
-      // it by more than the slack (or the first visible tile) moves it ------
+      // ---- lazy rescale: only a tile whose scores (scaled to log2 units)
+      // exceed the running max by more than the slack moves it (the first
+      // visible tile always does) --------------------------------------------
       float m0 = max3(s[nb][0][0], s[nb][0][1], s[nb][0][2]);
       m0 = max3(m0, s[nb][0][3], s[nb][1][0]);
 #pragma unroll
@@ -352,10 +348,9 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
         m0 = kb + 1 < NKB ? max3(m0, s[nb][kb][3], s[nb][kb + 1][0])
                           : fmaxf(m0, s[nb][kb][3]);
       }
-      const float thr = mc[nb] == kNegInf ? kNegInf : kRescaleSlack;
-      if (__any(m0 > thr)) [[unlikely]] {
-        const float base = mc[nb] == kNegInf ? 0.f : mc[nb];
-        const float mnew = fmaxf(mc[nb], quad_max(m0) + base);
+      // (scale > 0 commutes with the max; a masked score is -inf either way)
+      if (__any(m0 * qk_scale > mc[nb] + kRescaleSlack)) [[unlikely]] {
+        const float mnew = fmaxf(mc[nb], quad_max(m0) * qk_scale);
         // a query with no visible key yet keeps max -inf: no rescale (and
         // no -inf - -inf)
         const float alpha = mnew == mc[nb] ? 1.f : fast_exp2(mc[nb] - mnew);
@@ -363,19 +358,17 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
         lacc[nb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[nb][db] *= alpha;
-        const float shift = mnew == kNegInf ? 0.f : base - mnew;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[nb][kb] += shift;
-        const float ninit = mnew == kNegInf ? 0.f : -mnew;
-        sinit[nb] = f32x4_t{ninit, ninit, ninit, ninit};
       }
+      // every score of a query with max -inf is masked: any finite offset
+      // gives p = 0 (and -mc would be +inf)
+      const float nmc = mc[nb] == kNegInf ? 0.f : -mc[nb];
 #pragma unroll
       for (int t2 = 0; t2 < BN / 32; ++t2) {
         float p[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          p[r] = fast_exp2(s[nb][2 * t2][r]);
-          p[4 + r] = fast_exp2(s[nb][2 * t2 + 1][r]);
+          p[r] = fast_exp2(fmaf(s[nb][2 * t2][r], qk_scale, nmc));
+          p[4 + r] = fast_exp2(fmaf(s[nb][2 * t2 + 1][r], qk_scale, nmc));
         }
         const u32x4_t pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                             pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
