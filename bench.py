@@ -23,9 +23,15 @@ decode batch, the decoder-causal top-k, the paged prefill, the prefill shape
 at head size 128 and with 32 heads, and the single-sequence decode at
 position 8000 (cold and warm, from a captured graph).
 
+The `context` object holds the read bandwidth a compute-free streaming read
+over 4 GiB attains (attn_read_probe), against which the decode bandwidth can
+be read, and the GPU's clock levels, performance level, power and
+temperatures (sysfs) just before and after the timed steps.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
+import glob
 import hashlib
 import json
 import math
@@ -390,6 +396,79 @@ def bench_prefill_paged(torch, tas, pre, page_size, layout, n=20):
                 TFLOPs_paged=round(pre["flops"] / tp / 1e6, 1))
 
 
+def gpu_state(torch):
+    """Clock levels in use, performance level, power and temperatures of
+    cuda:0, read from sysfs (the state beside a measurement); None where the
+    files cannot be read."""
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        dev = (f"/sys/bus/pci/devices/{pr.pci_domain_id:04x}:"
+               f"{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0")
+    except Exception:
+        return None
+    if not os.path.isdir(dev):
+        return None
+
+    def read(path):
+        try:
+            with open(path) as f:
+                return f.read().strip()
+        except OSError:
+            return None
+
+    def level(name):
+        text = read(os.path.join(dev, name))
+        for ln in (text or "").splitlines():
+            if ln.rstrip().endswith("*"):
+                return ln.split(":", 1)[-1].rstrip("* ").strip()
+        return None
+
+    st = {"pci": os.path.basename(dev), "sclk": level("pp_dpm_sclk"),
+          "mclk": level("pp_dpm_mclk"), "fclk": level("pp_dpm_fclk"),
+          "performance_level": read(os.path.join(
+              dev, "power_dpm_force_performance_level"))}
+    for hw in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+        for name in ("power1_average", "power1_input"):
+            v = read(os.path.join(hw, name))
+            if v and "power_w" not in st:
+                st["power_w"] = round(int(v) * 1e-6, 1)
+        for tin in sorted(glob.glob(os.path.join(hw, "temp*_input"))):
+            v = read(tin)
+            lab = read(tin.replace("_input", "_label")) or os.path.basename(tin)
+            if v:
+                st[f"temp_{lab}_c"] = round(int(v) * 1e-3, 1)
+    return st
+
+
+def bench_read_probe(torch, tas, gib=4, reps=20):
+    """Attainable HBM read bandwidth: attn_read_probe over `gib` GiB (every
+    byte read once with 16-byte non-temporal loads) at three grid sizes,
+    `reps` back-to-back calls each between two events."""
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    by_wg = {}
+    for wg in (2048, 4096, 8192):
+        sink = torch.empty((wg, 4), dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            tas.attn_read_probe(buf, wg, sink=sink)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            tas.attn_read_probe(buf, wg, sink=sink)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        by_wg[str(wg)] = round(nbytes / us / 1e3, 1)
+    del buf
+    torch.cuda.empty_cache()
+    best = max(by_wg.values())
+    return dict(bytes=nbytes, GBps=best,
+                frac_of_hbm_peak=round(best / HBM_PEAK_GBPS, 4),
+                GBps_by_workgroups=by_wg)
+
+
 def cpu_baseline(dec, synth, budget_s):
     import numpy as np
     import oracle
@@ -473,7 +552,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         log(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): "
-            "the path has no multi-GPU component in this build.")
+            "the attention path here has no multi-GPU component.")
         sys.exit(2)
     import numpy as np
     import torch
@@ -522,12 +601,14 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
            for _ in range(args.steps)]
     log(f"timing {args.steps} steps ...")
+    state_before = gpu_state(torch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    state_after = gpu_state(torch)
     t_dec = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3
     t_pre = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3
     t_tk = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps * 1e-3
@@ -609,6 +690,11 @@ def main():
         secondary["decode_single_pos8000"] = bench_single_position(
             torch, tas, synth)
 
+    log("streaming-read probe over 4 GiB ...")
+    context = {"read_probe": bench_read_probe(torch, tas),
+               "gpu_state_before": state_before,
+               "gpu_state_after": state_after}
+
     traffic = committed_traffic("decode_ragged_b64_traffic.txt",
                                 "decode.hip")
     roofline = {
@@ -649,6 +735,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "context": context,
     }
     print(json.dumps(line), flush=True)
 

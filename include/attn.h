@@ -30,6 +30,9 @@
  *                 recent topk/2.
  *                 Source: the same page, further thoughts.
  *
+ * attn_read_probe is a measurement aid beside them: a streaming read that
+ * gives the bandwidth the memory system attains.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Pointers are DEVICE pointers (memory the caller allocated with hipMalloc
@@ -317,6 +320,24 @@ int attn_topk(const float *q, const float *k, const float *v, float *out,
 int attn_topk_causal(const float *q, const float *k, const float *v, float *out,
                      int32_t *idx_out, int b, int h, int n, int d, int topk,
                      void *stream);
+
+/* Streaming-read probe (a measurement aid, not part of the attention path):
+ * reads `bytes` of device memory at src once, with 16-byte non-temporal
+ * loads, to measure the read bandwidth the memory system actually delivers,
+ * the context for the decode kernels' bandwidth.
+ *
+ *   src         device, 16-byte aligned, `bytes` readable (may be NULL when
+ *               bytes = 0); bytes a multiple of 16.
+ *   workgroups  in [1, 65536]; workgroup w reads the 16-byte words
+ *               [w*per, min((w+1)*per, bytes/16)), per = ceil(bytes/16 /
+ *               workgroups).
+ *   sink        device, 16-byte aligned, sink_bytes >= 16 * workgroups;
+ *               receives in sink[w] (four uint32) the XOR of the words
+ *               workgroup w read (zero for an empty range), so that no load
+ *               can be dropped and the coverage can be checked.
+ * Errors: ATTN_E_ARG for a size, alignment or pointer outside the above. */
+int attn_read_probe(const void *src, size_t bytes, void *sink,
+                    size_t sink_bytes, int workgroups, void *stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

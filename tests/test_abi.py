@@ -352,6 +352,23 @@ def test_topk_empty_is_a_noop(fn):
     assert topk(fn, h=0) == OK
 
 
+def probe(**kw):
+    a = dict(src=P, bytes=1 << 20, sink=P, sink_bytes=16 * 64, wg=64,
+             stream=None)
+    a.update(kw)
+    return lib.attn_read_probe(a["src"], a["bytes"], a["sink"],
+                               a["sink_bytes"], a["wg"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(wg=0), dict(wg=65537), dict(bytes=17), dict(sink_bytes=16 * 63),
+    dict(sink=None), dict(src=None), dict(src=P + 4), dict(sink=P + 8),
+])
+def test_read_probe_rejects(kw):
+    assert probe(**kw) == E_ARG
+    assert "attn_read_probe" in lib.attn_last_error().decode()
+
+
 def test_python_binding_raises_with_reason():
     import torch
     q = torch.zeros(1, 2, 64)  # CPU tensor: rejected by the binding

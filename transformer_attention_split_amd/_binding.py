@@ -65,13 +65,15 @@ lib.attn_topk.restype = _i
 lib.attn_topk.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
 lib.attn_topk_causal.restype = _i
 lib.attn_topk_causal.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p]
+lib.attn_read_probe.restype = _i
+lib.attn_read_probe.argtypes = [_p, _sz, _p, _sz, _i, _p]
 
 EXPORTED = ("attn_status_str", "attn_last_error", "attn_abi_version",
             "attn_decode_workspace_bytes", "attn_decode", "attn_decode_append",
             "attn_decode_append_rope",
             "attn_decode_paged", "attn_prefill", "attn_prefill_paged",
             "attn_topk",
-            "attn_topk_causal")
+            "attn_topk_causal", "attn_read_probe")
 
 
 class AttnError(RuntimeError):
@@ -454,3 +456,29 @@ def attn_topk_causal(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     plus the best-scoring older ones. Arguments as ``attn_topk``; rows that
     keep fewer than ``topk`` keys pad ``idx_out`` with -1."""
     return _topk_call("attn_topk_causal", q, k, v, topk, out, idx_out, stream)
+
+
+# ----------------------------------------------------------------------------
+# Streaming-read probe (measurement aid)
+# ----------------------------------------------------------------------------
+def attn_read_probe(src: torch.Tensor, workgroups: int = 4096, *,
+                    sink: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Read every byte of the contiguous device tensor ``src`` once (its
+    size a multiple of 16 bytes). Returns ``sink``, int32 [workgroups, 4]:
+    row w is the XOR of the 16-byte words workgroup w read."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty((workgroups, 4), dtype=torch.int32,
+                           device=src.device)
+    elif not sink.is_contiguous() or sink.dtype != torch.int32 or \
+            sink.numel() < 4 * workgroups:
+        raise ValueError("sink must be contiguous int32 with >= 4*workgroups "
+                         "elements")
+    st = lib.attn_read_probe(_ptr(src), nbytes, _ptr(sink),
+                             sink.numel() * 4, int(workgroups),
+                             _stream_handle(stream))
+    _check(st, "attn_read_probe")
+    return sink

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "topk.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "topk.hip", "probe.hip"]
 
 # Per-source extra flags. The prefill kernel never lets a NaN reach its
 # arithmetic (rows past the valid length are not read; -inf is used for

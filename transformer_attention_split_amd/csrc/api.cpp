@@ -493,4 +493,24 @@ int attn_topk_causal(const float *q, const float *k, const float *v, float *out,
                    stream);
 }
 
+int attn_read_probe(const void *src, size_t bytes, void *sink,
+                    size_t sink_bytes, int workgroups, void *stream) {
+  const char *fn = "attn_read_probe";
+  if (workgroups < 1 || workgroups > 65536)
+    return fail(ATTN_E_ARG, "%s: workgroups=%d outside [1, 65536]", fn, workgroups);
+  if (bytes % 16 != 0)
+    return fail(ATTN_E_ARG, "%s: bytes=%zu is not a multiple of 16", fn, bytes);
+  if (sink_bytes < (size_t)16 * (size_t)workgroups)
+    return fail(ATTN_E_ARG, "%s: sink holds %zu bytes, needs 16 * %d", fn,
+                sink_bytes, workgroups);
+  if (!sink || (bytes > 0 && !src))
+    return fail(ATTN_E_ARG, "%s: null pointer", fn);
+  if (!aligned(src, 16) || !aligned(sink, 16))
+    return fail(ATTN_E_ARG, "%s: src and sink must be 16-byte aligned", fn);
+  hipError_t e = attn::launch_read_probe(src, bytes / 16, sink, workgroups,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
 }  // extern "C"

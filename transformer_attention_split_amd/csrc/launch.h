@@ -73,4 +73,9 @@ struct TopkArgs {
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 
+// Streaming-read probe over n16 16-byte words of src; sink holds one 16-byte
+// XOR per workgroup (1 <= workgroups <= 65536).
+hipError_t launch_read_probe(const void *src, size_t n16, void *sink,
+                             int workgroups, hipStream_t stream);
+
 }  // namespace attn
