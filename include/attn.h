@@ -248,8 +248,10 @@ int attn_decode_paged(int dtype, const void *q, const void *k_pages,
  *   out        [B][Hq][Lq][D]
  *   scale      finite and > 0 (binding default 1/sqrt(D)).
  * Requires 0 <= prefix_len, 0 <= Lq, prefix_len + Lq <= max_length.
- * Supported: D in {64, 128}; Hq % Hkv == 0; B, Hq <= 65535. Lq == 0 or
- * B == 0 is a no-op. */
+ * Supported: D in {64, 128}; Hq % Hkv == 0; B, Hq <= 65535;
+ * (prefix_len + Lq) * 2 * D < 2^31 (one kv head's rows are addressed with
+ * 32-bit byte offsets; ATTN_E_UNSUPPORTED beyond). Lq == 0 or B == 0 is a
+ * no-op. */
 int attn_prefill(int dtype, const void *q, const void *k_cache,
                  const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
                  int max_length, int Lq, int prefix_len, float scale,

@@ -258,6 +258,9 @@ def prefill(**kw):
     (dict(Lq=-1), E_ARG),
     (dict(prefix_len=-1), E_ARG),
     (dict(prefix_len=3073), E_ARG),     # prefix + Lq > max_length
+    # one kv head's rows past 2^31 bytes (32-bit offsets in the kernel)
+    (dict(D=128, max_length=1 << 23, prefix_len=(1 << 23) - 1024), E_UNSUP),
+    (dict(D=64, max_length=1 << 24, prefix_len=(1 << 24) - 1024), E_UNSUP),
     (dict(max_length=0), E_ARG),
     (dict(scale=float("nan")), E_ARG),
     (dict(scale=0.0), E_ARG),
@@ -297,6 +300,8 @@ def prefill_paged(**kw):
     (dict(layout=-1), E_ARG),
     (dict(max_blocks=1 << 20, page_size=4096), E_ARG),  # 2^32 rows
     (dict(max_blocks=63), E_ARG),      # prefix + Lq > max_blocks * page_size
+    (dict(D=128, page_size=4096, max_blocks=2048, num_pages=4,
+          prefix_len=(1 << 23) - 1024), E_UNSUP),  # rows past 2^31 bytes
     (dict(table=None), E_ARG),
     (dict(table=P + 2), E_ARG),
     (dict(dtype=F32), E_UNSUP),

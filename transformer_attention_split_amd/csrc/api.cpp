@@ -385,6 +385,11 @@ int prefill_check(const char *fn, int dtype, const void *q, const void *k,
   if (!fits({(double)B, (double)Hkv, (double)max_length, (double)D, 2.0}) ||
       !fits({(double)B, (double)Hq, (double)max_length, (double)D, 2.0}))
     return fail(ATTN_E_ARG, "%s: extents overflow", fn);
+  // The kernel addresses the rows [0, prefix_len + Lq) of one kv head with
+  // 32-bit byte offsets.
+  if (((long long)prefix_len + Lq) * D * 2 > 0x7fffffffLL)
+    return fail(ATTN_E_UNSUPPORTED, "%s: prefix_len+Lq=%lld rows of %d bytes exceed 2^31 bytes",
+                fn, (long long)prefix_len + Lq, 2 * D);
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(ATTN_E_ARG, "%s: scale must be finite and > 0", fn);
   if (B == 0 || Lq == 0) return ok();  // nothing is read or written
