@@ -400,3 +400,16 @@ def test_build_script_loads_without_the_package():
     assert "transformer_attention_split_amd" not in [
         ln.split()[1] for ln in text.splitlines()
         if ln.startswith(("import ", "from "))]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU: --gpus above 1 exits with a message before
+    touching a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr + r.stdout
+    assert r.stdout.strip() == ""  # no JSON line
