@@ -218,13 +218,17 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
 
   f32x4_t o[NB][NDB];
   f32x4_t lacc[NB];
-  float mc[NB];  // running max (log2 units), -inf before the first key
+  float mc[NB];   // running max (log2 units), -inf before the first key
+  float nmc[NB];  // exponent offset: -mc, 0 while mc = -inf
+  float thr[NB];  // raw score above which the max must move: (mc + slack) / scale
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
     for (int i = 0; i < NDB; ++i) o[nb][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     lacc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     mc[nb] = kNegInf;
+    nmc[nb] = 0.f;
+    thr[nb] = kNegInf;
   }
 
   // Loads: load jj of a tile fills LDS bytes [1024 jj, 1024 jj + 1024); lane
@@ -348,27 +352,29 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
         m0 = kb + 1 < NKB ? max3(m0, s[nb][kb][3], s[nb][kb + 1][0])
                           : fmaxf(m0, s[nb][kb][3]);
       }
-      // (scale > 0 commutes with the max; a masked score is -inf either way)
-      if (__any(m0 * qk_scale > mc[nb] + kRescaleSlack)) [[unlikely]] {
+      // (scale > 0 commutes with the max; a masked score is -inf and never
+      // passes the threshold, which is -inf before the first visible key)
+      if (__any(m0 > thr[nb])) [[unlikely]] {
         const float mnew = fmaxf(mc[nb], quad_max(m0) * qk_scale);
         // a query with no visible key yet keeps max -inf: no rescale (and
         // no -inf - -inf)
         const float alpha = mnew == mc[nb] ? 1.f : fast_exp2(mc[nb] - mnew);
         mc[nb] = mnew;
+        // every score of a query with max -inf is masked: any finite offset
+        // gives p = 0 (and -mc would be +inf)
+        nmc[nb] = mnew == kNegInf ? 0.f : -mnew;
+        thr[nb] = (mnew + kRescaleSlack) / qk_scale;
         lacc[nb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) o[nb][db] *= alpha;
       }
-      // every score of a query with max -inf is masked: any finite offset
-      // gives p = 0 (and -mc would be +inf)
-      const float nmc = mc[nb] == kNegInf ? 0.f : -mc[nb];
 #pragma unroll
       for (int t2 = 0; t2 < BN / 32; ++t2) {
         float p[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          p[r] = fast_exp2(fmaf(s[nb][2 * t2][r], qk_scale, nmc));
-          p[4 + r] = fast_exp2(fmaf(s[nb][2 * t2 + 1][r], qk_scale, nmc));
+          p[r] = fast_exp2(fmaf(s[nb][2 * t2][r], qk_scale, nmc[nb]));
+          p[4 + r] = fast_exp2(fmaf(s[nb][2 * t2 + 1][r], qk_scale, nmc[nb]));
         }
         const u32x4_t pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                             pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
