@@ -73,7 +73,7 @@ typedef enum attn_dtype {
 } attn_dtype;
 
 /* Static description of a status code. Never NULL. */
-const char *attn_status_str(int status);
+const char *attn_status_str(attn_status status);
 
 /* Human-readable reason for the last nonzero status returned on the calling
  * thread ("" if none). Valid until the next call on the same thread. */
@@ -125,7 +125,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D,
  *              Calls that may overlap need distinct workspaces.
  * Supported: D in {64, 128}; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8};
  * B, Hkv <= 65535. B == 0 is a no-op. */
-int attn_decode(int dtype, const void *q, const void *k_cache,
+attn_status attn_decode(attn_dtype dtype, const void *q, const void *k_cache,
                 const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
                 int max_length, int position_id, const int32_t *seq_lens,
                 float scale, int split_rows, void *workspace,
@@ -153,7 +153,7 @@ int attn_decode(int dtype, const void *q, const void *k_cache,
  * and the reads of that row do not race). k_new / v_new must not alias the
  * caches or out. ATTN_E_ARG if B > 0 and k_new or v_new is NULL or not
  * 16-byte aligned. */
-int attn_decode_append(int dtype, const void *q, const void *k_new,
+attn_status attn_decode_append(attn_dtype dtype, const void *q, const void *k_new,
                        const void *v_new, void *k_cache, void *v_cache,
                        void *out, int B, int Hq, int Hkv, int D, int max_length,
                        int position_id, const int32_t *seq_lens, float scale,
@@ -178,7 +178,7 @@ int attn_decode_append(int dtype, const void *q, const void *k_new,
  * key and v_new unchanged, and the rotated query attends. Everything else is
  * attn_decode_append. ATTN_E_ARG if B > 0 and a table pointer is NULL or
  * misaligned. */
-int attn_decode_append_rope(int dtype, const void *q, const void *k_new,
+attn_status attn_decode_append_rope(attn_dtype dtype, const void *q, const void *k_new,
                             const void *v_new, const float *rope_cos,
                             const float *rope_sin, void *k_cache, void *v_cache,
                             void *out, int B, int Hq, int Hkv, int D,
@@ -223,10 +223,10 @@ typedef enum attn_page_layout {
  * D = 128, 64 at D = 64) up to 65536; Hq/Hkv in {1, 2, 4, 8}; B, Hkv <=
  * 65535; max_blocks * page_size < 2^31. ATTN_E_ARG for page_size, max_blocks
  * or num_pages < 1, an unknown page_layout or a null block_table with B > 0. */
-int attn_decode_paged(int dtype, const void *q, const void *k_pages,
+attn_status attn_decode_paged(attn_dtype dtype, const void *q, const void *k_pages,
                       const void *v_pages, const int32_t *block_table,
                       int max_blocks, int page_size, int num_pages,
-                      int page_layout, void *out,
+                      attn_page_layout page_layout, void *out,
                       int B, int Hq, int Hkv, int D, int position_id,
                       const int32_t *seq_lens, float scale, int split_rows,
                       void *workspace, size_t workspace_bytes, void *stream);
@@ -252,7 +252,7 @@ int attn_decode_paged(int dtype, const void *q, const void *k_pages,
  * (prefix_len + Lq) * 2 * D < 2^31 (one kv head's rows are addressed with
  * 32-bit byte offsets; ATTN_E_UNSUPPORTED beyond). Lq == 0 or B == 0 is a
  * no-op. */
-int attn_prefill(int dtype, const void *q, const void *k_cache,
+attn_status attn_prefill(attn_dtype dtype, const void *q, const void *k_cache,
                  const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
                  int max_length, int Lq, int prefix_len, float scale,
                  void *stream);
@@ -274,10 +274,10 @@ int attn_prefill(int dtype, const void *q, const void *k_cache,
  * key tile, 4096 / D rows (64 at D = 64, 32 at D = 128), up to 65536;
  * max_blocks * page_size < 2^31. ATTN_E_UNSUPPORTED for another page_size;
  * ATTN_E_ARG as attn_decode_paged for the table arguments. */
-int attn_prefill_paged(int dtype, const void *q, const void *k_pages,
+attn_status attn_prefill_paged(attn_dtype dtype, const void *q, const void *k_pages,
                        const void *v_pages, const int32_t *block_table,
                        int max_blocks, int page_size, int num_pages,
-                       int page_layout, void *out, int B, int Hq, int Hkv, int D,
+                       attn_page_layout page_layout, void *out, int B, int Hq, int Hkv, int D,
                        int Lq, int prefix_len, float scale, void *stream);
 
 /* --------------------------------------------------------------------------
@@ -299,7 +299,7 @@ int attn_prefill_paged(int dtype, const void *q, const void *k_pages,
  * b·h·ceil(n/16) <= 2^23 (one workgroup per 16 rows). b == 0 or h == 0 is a
  * no-op. Inputs must be finite (a NaN or infinite input leaves the
  * selection unspecified). */
-int attn_topk(const float *q, const float *k, const float *v, float *out,
+attn_status attn_topk(const float *q, const float *k, const float *v, float *out,
               int32_t *idx_out, int b, int h, int n, int d, int topk,
               void *stream);
 
@@ -319,7 +319,7 @@ int attn_topk(const float *q, const float *k, const float *v, float *out,
  * Arguments, layouts, precision, limits and errors are those of attn_topk.
  * idx_out (optional) [b][h][n][topk] receives S_i in ascending order,
  * followed by -1 in the topk - |S_i| slots of rows with i+1 < topk. */
-int attn_topk_causal(const float *q, const float *k, const float *v, float *out,
+attn_status attn_topk_causal(const float *q, const float *k, const float *v, float *out,
                      int32_t *idx_out, int b, int h, int n, int d, int topk,
                      void *stream);
 
@@ -338,7 +338,7 @@ int attn_topk_causal(const float *q, const float *k, const float *v, float *out,
  *               workgroup w read (zero for an empty range), so that no load
  *               can be dropped and the coverage can be checked.
  * Errors: ATTN_E_ARG for a size, alignment or pointer outside the above. */
-int attn_read_probe(const void *src, size_t bytes, void *sink,
+attn_status attn_read_probe(const void *src, size_t bytes, void *sink,
                     size_t sink_bytes, int workgroups, void *stream);
 
 #ifdef __cplusplus

@@ -232,3 +232,39 @@ def test_decode_empty_batch_is_noop():
     k = torch.empty(0, 1, 8, 64, device="cuda")
     out = tas.attn_decode(q, k, k.clone(), position_id=0)
     assert out.shape == (0, 4, 64)
+
+
+def test_decode_on_side_stream_keeps_its_workspace():
+    # The binding allocates the workspace (and out) itself on the current
+    # stream while the kernels run on `stream`. A long matrix product queued
+    # first keeps the side stream busy; the binding then returns and the
+    # test allocates and overwrites memory of the same size on the current
+    # stream. Unless the binding recorded the side stream's use, the
+    # allocator can hand that block over while split and combine still use
+    # it, and the output is corrupted.
+    inp = synth.decode_ragged(77, B=8, Hq=8, Hkv=2, D=128, max_length=4096,
+                              dtype="bf16")
+    q = to_dev(inp.q, "bf16")
+    k = to_dev(inp.k_cache, "bf16")
+    v = to_dev(inp.v_cache, "bf16")
+    lens = torch.from_numpy(inp.seq_lens.astype(np.int32)).cuda()
+    need = tas.attn_decode_workspace_bytes(8, 8, 2, 128, 4096, 128)
+    ref = oracle_of(inp)
+    side = torch.cuda.Stream()
+    big = torch.randn(4096, 4096, device="cuda")
+    torch.cuda.synchronize()
+    say("decode on a side stream, allocations on the current stream")
+    for stream_arg in (side, side.cuda_stream):
+        with torch.cuda.stream(side):
+            for _ in range(8):
+                big = big @ big * 1e-3
+        out = tas.attn_decode(q, k, v, seq_lens=lens, scale=inp.scale,
+                              split_rows=128, stream=stream_arg)
+        junk = [torch.full((need,), 255, dtype=torch.uint8,
+                           device="cuda") for _ in range(4)]
+        junk.append(torch.full(out.shape, float("nan"), dtype=out.dtype,
+                               device="cuda"))
+        torch.cuda.synchronize()
+        err = max_abs_err(to_host64(out), ref)
+        assert err <= tol("bf16"), err
+        del junk

@@ -75,10 +75,20 @@ def test_prefill_paged_prefix3072(layout, page_size):
     (2, 2, 2, 200, 333, 17, 64),   # ragged everything, several sequences
 ])
 def test_prefill_paged_shapes(D, layout, B, Hq, Hkv, Lq, prefix, extra, ps):
-    if ps % (4096 // D):
-        pytest.skip("page size not a multiple of the D=64 tile (64 rows)")
     inp = synth.prefill(2000 + Lq + prefix, B, Hq, Hkv, D, Lq, prefix,
                         max_length=prefix + Lq + extra, dtype="bf16")
+    if ps % (4096 // D):
+        # pages must hold whole key tiles (4096 / D rows): the call is
+        # refused before any launch
+        k, v = _padded(inp, ps)
+        kp, vp, table = synth.paginate(k, v, ps, 82 + Lq, layout=layout)
+        with pytest.raises(tas.AttnArgError) as ei:
+            tas.attn_prefill_paged(
+                to_dev(inp.q, "bf16"), to_dev(kp, "bf16"), to_dev(vp, "bf16"),
+                torch.from_numpy(table).cuda(), prefix_len=inp.prefix_len,
+                layout=layout, scale=inp.scale)
+        assert ei.value.status == tas.ATTN_E_UNSUPPORTED
+        return
     say(f"prefill_paged D={D} B={B} Hq={Hq} Hkv={Hkv} Lq={Lq} prefix={prefix} "
         f"page={ps} {layout}")
     check_paged(inp, ps, layout, 82 + Lq)

@@ -27,7 +27,14 @@ def run(q, k, v, topk):
     return out.cpu().numpy().astype(np.float64), idx.cpu().numpy()
 
 
-def check(q, k, v, topk, out, idx):
+def check(q, k, v, topk, out, idx, ulp_allowance=False):
+    """Exact index sets (outside ambiguous rows) and max abs error <= 1e-4.
+
+    ulp_allowance: the outlier-key tests have outputs of magnitude ~1e5,
+    where neighbouring fp32 values are ~0.008 apart and no fp32 result can
+    lie within 1e-4 of the fp64 value; there one fp32 unit in the last place
+    of the value is allowed on top of the absolute bound. Everywhere else
+    the bound is the plain max abs error."""
     ref, ref_idx, gap = oracle.topk_sparse(q, k, v, topk, return_details=True)
     b, h, n, _ = q.shape
     ambiguous = 0
@@ -50,12 +57,12 @@ def check(q, k, v, topk, out, idx):
                     assert s[i, sel].min() >= s[i, ~sel].max() - eps[i]
                 ref[bb, hh, i] = s[i, got[i]] @ v[bb, hh, got[i]].astype(
                     np.float64)
-    # the fp64 result is rounded once to fp32: beyond the absolute
-    # tolerance allow that rounding (half an fp32 ulp of the value, at most
-    # 2^-24 relative; one ulp is allowed here)
     err = max_abs_err(out, ref)
-    excess = np.max(np.abs(out - ref) - 2.0 ** -23 * np.abs(ref))
-    assert excess <= F32_TOL, (err, excess)
+    if ulp_allowance:
+        excess = np.max(np.abs(out - ref) - 2.0 ** -23 * np.abs(ref))
+        assert excess <= F32_TOL, (err, excess)
+    else:
+        assert err <= F32_TOL, err
     return ambiguous
 
 
@@ -113,7 +120,7 @@ def test_topk_one_outlier_key_squeezes_the_score_range(topk):
     k[:, :, 17] *= np.float32(1e5)
     say(f"topk outlier key, topk={topk}")
     out, idx = run(inp.q, k, inp.v, topk)
-    check(inp.q, k, inp.v, topk, out, idx)
+    check(inp.q, k, inp.v, topk, out, idx, ulp_allowance=True)
 
 
 def test_topk_zero_queries_and_signed_zeros():

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import F32_TOL, say, to_dev
+from gpu_helpers import F32_TOL, max_abs_err, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +30,10 @@ def run(q, k, v, topk):
     return out.cpu().numpy().astype(np.float64), idx.cpu().numpy()
 
 
-def check(q, k, v, topk, out, idx):
+def check(q, k, v, topk, out, idx, ulp_allowance=False):
+    """Exact index sets (outside ambiguous rows) and max abs error <= 1e-4;
+    ulp_allowance adds one fp32 unit in the last place of the value, for the
+    outlier-key outputs (~1e5) that no fp32 value can hold to 1e-4."""
     ref, ref_idx, gap = oracle.topk_causal_sparse(q, k, v, topk,
                                                   return_details=True)
     b, h, n, _ = q.shape
@@ -57,9 +60,12 @@ def check(q, k, v, topk, out, idx):
                 assert s[i, :i + 1 - r][old].min() >= \
                     s[i, :i + 1 - r][~old].max() - eps[i]
                 ref[bb, hh, i] = s[i, sel] @ v[bb, hh, sel].astype(np.float64)
-    # one fp32 rounding of the fp64 result is allowed beyond the tolerance
-    excess = np.max(np.abs(out - ref) - 2.0 ** -23 * np.abs(ref))
-    assert excess <= F32_TOL, excess
+    err = max_abs_err(out, ref)
+    if ulp_allowance:
+        excess = np.max(np.abs(out - ref) - 2.0 ** -23 * np.abs(ref))
+        assert excess <= F32_TOL, (err, excess)
+    else:
+        assert err <= F32_TOL, err
     return ambiguous
 
 
@@ -88,8 +94,7 @@ def test_topk_causal_k_equals_n_is_lower_triangular():
     out, idx = run(inp.q, inp.k, inp.v, 200)
     q, k, v = (x.astype(np.float64) for x in (inp.q, inp.k, inp.v))
     ref = np.tril(q @ np.swapaxes(k, -1, -2)) @ v
-    excess = np.max(np.abs(out - ref) - 2.0 ** -23 * np.abs(ref))
-    assert excess <= F32_TOL
+    assert max_abs_err(out, ref) <= F32_TOL
     for i in range(200):
         assert np.array_equal(idx[0, 0, i, :i + 1], np.arange(i + 1))
         assert np.all(idx[0, 0, i, i + 1:] == -1)
@@ -107,8 +112,7 @@ def test_topk_causal_exact_ties_lower_index_wins():
         ref, ref_idx, _ = oracle.topk_causal_sparse(inp.q, k, inp.v, topk,
                                                     return_details=True)
         assert np.array_equal(idx, ref_idx), topk
-        excess = np.max(np.abs(out - ref) - 2.0 ** -23 * np.abs(ref))
-        assert excess <= F32_TOL
+        assert max_abs_err(out, ref) <= F32_TOL
 
 
 @pytest.mark.parametrize("topk", [5, 64, 300])
@@ -118,7 +122,7 @@ def test_topk_causal_outlier_key_forces_exact_ranking(topk):
     k[:, :, 17] *= np.float32(1e5)
     say(f"topk_causal outlier key, topk={topk}")
     out, idx = run(inp.q, k, inp.v, topk)
-    check(inp.q, k, inp.v, topk, out, idx)
+    check(inp.q, k, inp.v, topk, out, idx, ulp_allowance=True)
 
 
 def test_topk_causal_zero_queries_take_the_oldest_keys():

@@ -7,9 +7,11 @@ something fixed independently of it:
 * closed forms (single row, uniform weights, constant V, k=1, k=n);
 * library routines the pages themselves call: PyTorch's CPU
   ``scaled_dot_product_attention`` in float64 (sliced cache with
-  ``enable_gqa``, the original full-cache bool mask, ``is_causal``),
-  ``torch.topk`` + ``scatter`` and ``matmul``;
-* invariants the pages state (slice == mask, batched == per-head loop,
+  ``enable_gqa``, the original full-cache bool mask, ``is_causal``);
+* the definitions in an independent form: all heads in one batched product
+  with the causal condition applied by selection; top-k as a keep mask
+  ("score >= the row's k-th largest") times v;
+* invariants the pages state (slice == mask, batched == per-head results,
   GQA == MHA with repeated K/V, position 0 == identity);
 * brute force over all k-subsets for top-k on tiny inputs.
 
@@ -500,25 +502,27 @@ def test_prefill_row_equals_decode_at_prefix_plus_i():
         np.testing.assert_allclose(out[:, :, i], dec, rtol=0, atol=1e-14)
 
 
-def test_prefill_equals_per_head_loop_token_major():
-    # The problem section's per-head loop over token-major tensors
-    # Q [seq, H, d], K_full/V_full [total, H, d], joined with torch.cat.
+def test_prefill_token_major_all_heads_at_once():
+    # "step14_3 — batched attention", solution section: every head in one
+    # batched product over token-major Q [seq, H, d], K/V [total, H, d], the
+    # bottom-right causal condition (new token t sees key s iff s <= prefix
+    # + t) applied by selection, and the heads' outputs side by side in
+    # [seq, H*d]. Written as one batched contraction per step, not per head.
     rng = np.random.default_rng(9)
     H, d, Lq, prefix = 6, 16, 9, 13
     T = prefix + Lq
-    Q = _t(rng.standard_normal((Lq, H, d)))
-    Kf = _t(rng.standard_normal((T, H, d)))
-    Vf = _t(rng.standard_normal((T, H, d)))
-    mask = ~_bottom_right_mask(Lq, prefix)
-    outs = []
-    for h in range(H):
-        sc = torch.matmul(Q[:, h, :], Kf[:, h, :].T) / math.sqrt(d)
-        sc = sc.masked_fill(mask, float("-inf"))
-        outs.append(torch.matmul(torch.softmax(sc, dim=-1), Vf[:, h, :]))
-    ref = torch.cat(outs, dim=-1).numpy()                  # [Lq, H*d]
-    out = oracle.prefill(Q.transpose(0, 1)[None].numpy(),
-                         Kf.transpose(0, 1)[None].numpy(),
-                         Vf.transpose(0, 1)[None].numpy(), prefix)
+    Q = rng.standard_normal((Lq, H, d))
+    Kf = rng.standard_normal((T, H, d))
+    Vf = rng.standard_normal((T, H, d))
+    sc = torch.einsum("thd,shd->hts", _t(Q), _t(Kf)) / math.sqrt(d)
+    allowed = torch.arange(T)[None, :] <= prefix + torch.arange(Lq)[:, None]
+    sc = torch.where(allowed[None], sc, torch.tensor(float("-inf"),
+                                                     dtype=sc.dtype))
+    w = torch.exp(sc - sc.amax(dim=-1, keepdim=True))
+    w = w / w.sum(dim=-1, keepdim=True)
+    ref = torch.einsum("hts,shd->thd", w, _t(Vf)).reshape(Lq, H * d).numpy()
+    out = oracle.prefill(Q.transpose(1, 0, 2)[None], Kf.transpose(1, 0, 2)[None],
+                         Vf.transpose(1, 0, 2)[None], prefix)
     out_tm = out[0].transpose(1, 0, 2).reshape(Lq, H * d)
     np.testing.assert_allclose(out_tm, ref, rtol=0, atol=1e-12)
 
@@ -561,20 +565,26 @@ def test_topk_k1_is_max_score_times_argmax_row():
     np.testing.assert_allclose(out, ref.numpy(), rtol=0, atol=1e-12)
 
 
-def test_topk_matches_page_topk_scatter_form():
-    # The page's code, with torch.topk + zeros_like.scatter + matmul, on
-    # data without ties (torch.topk's order among equal scores is unfixed).
+def test_topk_keep_mask_product_form():
+    # c2psa page, core implementation §2: keep each row's k largest scores,
+    # zero the rest, multiply by v (no scale, no softmax). Here the kept set
+    # is a boolean mask "score >= the row's k-th largest score" (tie-free
+    # random data, so the mask holds exactly k entries) and the product is
+    # the masked score matrix times v.
     rng = np.random.default_rng(14)
     q = rng.standard_normal((2, 3, 64, 16)).astype(np.float32)
     k = rng.standard_normal((2, 3, 64, 16)).astype(np.float32)
     v = rng.standard_normal((2, 3, 64, 16)).astype(np.float32)
-    attn = torch.matmul(_t(q), _t(k).transpose(-2, -1))
-    val, idx = torch.topk(attn, k=10, dim=-1)
-    sparse = torch.zeros_like(attn).scatter(-1, idx, val)
-    ref = torch.matmul(sparse, _t(v)).numpy()
-    out, myidx, _ = oracle.topk_sparse(q, k, v, 10, return_details=True)
+    kk = 10
+    s64 = q.astype(np.float64) @ np.swapaxes(k.astype(np.float64), -1, -2)
+    kth = -np.partition(-s64, kk - 1, axis=-1)[..., kk - 1:kk]
+    keep = s64 >= kth
+    assert np.all(keep.sum(axis=-1) == kk)
+    ref = np.where(keep, s64, 0.0) @ v.astype(np.float64)
+    out, myidx, _ = oracle.topk_sparse(q, k, v, kk, return_details=True)
     np.testing.assert_allclose(out, ref, rtol=0, atol=1e-11)
-    assert np.array_equal(np.sort(idx.numpy(), axis=-1), myidx)
+    kept_idx = np.nonzero(keep)[-1].reshape(2, 3, 64, kk)
+    assert np.array_equal(kept_idx, myidx)
 
 
 def test_topk_brute_force_over_all_subsets():
@@ -720,29 +730,44 @@ def test_topk_causal_k1_is_causal_max_times_its_row():
 
 
 @pytest.mark.parametrize("topk", [2, 7, 10, 16])
-def test_topk_causal_matches_masked_topk_scatter_plus_recent_band(topk):
-    # The page's torch.topk + scatter form applied to the older keys only
-    # (later keys masked to -inf), plus the band of the r most recent
-    # scores; rows with i+1 <= topk take the plain lower triangle. Data
-    # without ties.
+def test_topk_causal_keep_mask_form(topk):
+    # Reading of the c2psa page's further thoughts as a keep mask: a row with
+    # i+1 <= topk keeps its whole lower triangle; a longer row keeps its r
+    # most recent keys (i-r, i] and, among the older keys j <= i-r, those
+    # scoring at least the (topk-r)-th largest older score (tie-free data);
+    # the output is the masked score matrix times v.
     rng = np.random.default_rng(44)
     n = 40
     q = rng.standard_normal((2, 2, n, 16)).astype(np.float32)
     k = rng.standard_normal((2, 2, n, 16)).astype(np.float32)
     v = rng.standard_normal((2, 2, n, 16)).astype(np.float32)
     r = topk // 2
-    s = torch.matmul(_t(q), _t(k).transpose(-2, -1))
-    ii = torch.arange(n)[:, None]
-    jj = torch.arange(n)[None, :]
-    older = s.masked_fill(jj > ii - r, float("-inf"))
-    val, idx = torch.topk(older, k=topk - r, dim=-1)
-    sparse = torch.zeros_like(s).scatter(-1, idx, val)
-    sparse = torch.where((jj <= ii) & (jj > ii - r), s, sparse)
-    sparse = torch.where(ii + 1 <= topk, torch.tril(s), sparse)
-    ref = torch.matmul(sparse, _t(v)).numpy()
+    s64 = q.astype(np.float64) @ np.swapaxes(k.astype(np.float64), -1, -2)
+    ii = np.arange(n)[:, None]
+    jj = np.arange(n)[None, :]
+    older = jj <= ii - r
+    keep = np.zeros(s64.shape, bool)
+    for i in range(n):
+        if i + 1 <= topk:
+            keep[..., i, :i + 1] = True
+            continue
+        cand = s64[..., i, :i - r + 1]
+        kth = -np.partition(-cand, topk - r - 1, axis=-1)[..., topk - r - 1]
+        keep[..., i, :i - r + 1] = cand >= kth[..., None]
+        keep[..., i, i - r + 1:i + 1] = True
+    assert np.all(keep.sum(-1) == np.minimum(topk, np.arange(n) + 1))
+    assert not np.any(keep & (jj > ii))
+    assert np.all(keep[..., (jj <= ii) & ~older & (ii + 1 > topk)])
+    ref = np.where(keep, s64, 0.0) @ v.astype(np.float64)
     out, myidx, gap = oracle.topk_causal_sparse(q, k, v, topk,
                                                 return_details=True)
     np.testing.assert_allclose(out, ref, rtol=0, atol=1e-11)
+    for i in range(n):
+        c = min(topk, i + 1)
+        got = myidx[..., i, :c]
+        assert np.array_equal(got, np.nonzero(keep[..., i, :])[-1].reshape(
+            got.shape))
+        assert np.all(myidx[..., i, c:] == -1)
     assert np.all(np.isinf(gap[..., :topk])) and np.all(gap[..., topk:] > 0)
 
 
@@ -769,12 +794,13 @@ def test_topk_causal_rows_respect_order_and_recency():
 def test_fp32_accumulation_is_not_enough_for_topk_tolerance():
     # Why the kernel accumulates top-k scores and outputs in fp64: on the
     # C2PSA shape an fp32-accumulated path misses the 1e-4 fp32 tolerance.
+    # (fp32 scores, keep mask "score >= the row's 64th largest fp32 score",
+    # fp32 product of the masked scores with v)
     inp = synth.topk(5, 4, 3, 512, 64, 64)
     q, k, v = (torch.from_numpy(x) for x in (inp.q, inp.k, inp.v))
     attn = torch.matmul(q, k.transpose(-2, -1))
-    val, idx = torch.topk(attn, k=64, dim=-1)
-    sparse = torch.zeros_like(attn).scatter(-1, idx, val)
-    out32 = torch.matmul(sparse, v).double().numpy()
+    kth = attn.sort(dim=-1, descending=True).values[..., 63:64]
+    out32 = torch.matmul(torch.where(attn >= kth, attn, 0.0), v).double().numpy()
     ref = oracle.topk_sparse(inp.q, inp.k, inp.v, 64)
     assert np.max(np.abs(out32 - ref)) > 1e-4
     # while rounding the exact result to fp32 alone stays well inside it

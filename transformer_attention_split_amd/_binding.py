@@ -100,11 +100,36 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream_handle(stream) -> Optional[int]:
+def _resolve_stream(stream) -> torch.cuda.Stream:
+    """The stream the kernels are enqueued on, as a torch stream object:
+    the current stream for None, the object itself for a torch stream, and
+    an ExternalStream around a raw hipStream_t handle (int) or an object with
+    a ``cuda_stream`` attribute."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
     h = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    return h or None
+    if not h:
+        return torch.cuda.default_stream()
+    return torch.cuda.ExternalStream(h)
+
+
+def _handle(s: torch.cuda.Stream) -> Optional[int]:
+    return s.cuda_stream or None
+
+
+def _guard(s: torch.cuda.Stream, *owned: Optional[torch.Tensor]) -> None:
+    """Tensors this wrapper allocated (workspace, output, ...) come from the
+    caching allocator on the current stream. When the kernels run on another
+    stream, record that use: otherwise, once the wrapper drops its reference,
+    the allocator may hand the memory to the next allocation on the current
+    stream while the kernels still read or write it."""
+    if s == torch.cuda.current_stream(s.device):
+        return
+    for t in owned:
+        if t is not None:
+            t.record_stream(s)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -157,8 +182,10 @@ def _decode_args(q, k_cache, v_cache, position_id, seq_lens, scale,
             raise ValueError("seq_lens must be int32 [B]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    owned = []
     if out is None:
         out = torch.empty_like(q)
+        owned.append(out)
     else:
         _need_dense("out", out, 3)
         if out.shape != q.shape or out.dtype != q.dtype:
@@ -167,7 +194,8 @@ def _decode_args(q, k_cache, v_cache, position_id, seq_lens, scale,
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8,
                                 device=q.device)
-    return B, Hq, Hkv, D, max_length, float(scale), out, workspace
+        owned.append(workspace)
+    return B, Hq, Hkv, D, max_length, float(scale), out, workspace, owned
 
 
 def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -180,16 +208,17 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """Single-token decode. q [B,Hq,D]; caches [B,Hkv,max_length,D];
     exactly one of ``position_id`` (rows [0, position_id]) or ``seq_lens``
     (int32 [B] on the GPU, rows [0, seq_lens[b])). Returns out [B,Hq,D]."""
-    B, Hq, Hkv, D, max_length, scale, out, workspace = _decode_args(
+    B, Hq, Hkv, D, max_length, scale, out, workspace, owned = _decode_args(
         q, k_cache, v_cache, position_id, seq_lens, scale, split_rows, out,
         workspace)
+    s = _resolve_stream(stream)
     st = lib.attn_decode(_dtype_code(q), _ptr(q), _ptr(k_cache),
                          _ptr(v_cache), _ptr(out), B, Hq, Hkv, D, max_length,
                          -1 if position_id is None else int(position_id),
                          _ptr(seq_lens), scale, int(split_rows),
-                         _ptr(workspace), workspace.numel(),
-                         _stream_handle(stream))
+                         _ptr(workspace), workspace.numel(), _handle(s))
     _check(st, "attn_decode")
+    _guard(s, *owned)
     return out
 
 
@@ -205,20 +234,22 @@ def attn_decode_append(q: torch.Tensor, k_new: torch.Tensor,
     """Fused append + decode: k_new / v_new [B,Hkv,D] are stored at row
     position_id (or seq_lens[b]-1) of the caches, which are updated in place,
     and the result equals attn_decode on the updated caches."""
-    B, Hq, Hkv, D, max_length, scale, out, workspace = _decode_args(
+    B, Hq, Hkv, D, max_length, scale, out, workspace, owned = _decode_args(
         q, k_cache, v_cache, position_id, seq_lens, scale, split_rows, out,
         workspace)
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         _need_dense(name, t, 3)
         if tuple(t.shape) != (B, Hkv, D) or t.dtype != q.dtype:
             raise ValueError(f"{name} must be [{B},{Hkv},{D}] {q.dtype}")
+    s = _resolve_stream(stream)
     st = lib.attn_decode_append(
         _dtype_code(q), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
         _ptr(v_cache), _ptr(out), B, Hq, Hkv, D, max_length,
         -1 if position_id is None else int(position_id), _ptr(seq_lens),
         scale, int(split_rows), _ptr(workspace), workspace.numel(),
-        _stream_handle(stream))
+        _handle(s))
     _check(st, "attn_decode_append")
+    _guard(s, *owned)
     return out
 
 
@@ -236,7 +267,7 @@ def attn_decode_append_rope(q: torch.Tensor, k_new: torch.Tensor,
     fp32 cos / sin rows [B,D] of each sequence's current position
     (rotate-half pairs j, j+D/2), the rotated key and v_new are stored as in
     ``attn_decode_append`` and the rotated query attends."""
-    B, Hq, Hkv, D, max_length, scale, out, workspace = _decode_args(
+    B, Hq, Hkv, D, max_length, scale, out, workspace, owned = _decode_args(
         q, k_cache, v_cache, position_id, seq_lens, scale, split_rows, out,
         workspace)
     for name, t in (("k_new", k_new), ("v_new", v_new)):
@@ -247,13 +278,15 @@ def attn_decode_append_rope(q: torch.Tensor, k_new: torch.Tensor,
         _need_dense(name, t, 2)
         if tuple(t.shape) != (B, D) or t.dtype != torch.float32:
             raise ValueError(f"{name} must be float32 [{B},{D}]")
+    s = _resolve_stream(stream)
     st = lib.attn_decode_append_rope(
         _dtype_code(q), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cos),
         _ptr(sin), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, Hq, Hkv, D,
         max_length, -1 if position_id is None else int(position_id),
         _ptr(seq_lens), scale, int(split_rows), _ptr(workspace),
-        workspace.numel(), _stream_handle(stream))
+        workspace.numel(), _handle(s))
     _check(st, "attn_decode_append_rope")
+    _guard(s, *owned)
     return out
 
 
@@ -300,8 +333,10 @@ def attn_decode_paged(q: torch.Tensor, k_pages: torch.Tensor,
             raise ValueError("seq_lens must be int32 [B]")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    owned = []
     if out is None:
         out = torch.empty_like(q)
+        owned.append(out)
     else:
         _need_dense("out", out, 3)
         if out.shape != q.shape or out.dtype != q.dtype:
@@ -311,14 +346,17 @@ def attn_decode_paged(q: torch.Tensor, k_pages: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8,
                                 device=q.device)
+        owned.append(workspace)
+    s = _resolve_stream(stream)
     st = lib.attn_decode_paged(
         _dtype_code(q), _ptr(q), _ptr(k_pages), _ptr(v_pages),
         _ptr(block_table), max_blocks, page_size, num_pages, code, _ptr(out),
         B, Hq,
         Hkv, D, -1 if position_id is None else int(position_id),
         _ptr(seq_lens), float(scale), int(split_rows), _ptr(workspace),
-        workspace.numel(), _stream_handle(stream))
+        workspace.numel(), _handle(s))
     _check(st, "attn_decode_paged")
+    _guard(s, *owned)
     return out
 
 
@@ -345,17 +383,19 @@ def attn_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         raise ValueError("cache shape does not match q")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    owned = None
     if out is None:
-        out = torch.empty_like(q)
+        out = owned = torch.empty_like(q)
     else:
         _need_dense("out", out, 4)
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("out must match q's shape and dtype")
+    s = _resolve_stream(stream)
     st = lib.attn_prefill(_dtype_code(q), _ptr(q), _ptr(k_cache),
                           _ptr(v_cache), _ptr(out), B, Hq, Hkv, D, max_length,
-                          Lq, int(prefix_len), float(scale),
-                          _stream_handle(stream))
+                          Lq, int(prefix_len), float(scale), _handle(s))
     _check(st, "attn_prefill")
+    _guard(s, owned)
     return out
 
 
@@ -392,18 +432,21 @@ def attn_prefill_paged(q: torch.Tensor, k_pages: torch.Tensor,
         raise ValueError("page, block-table and query shapes do not match")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
+    owned = None
     if out is None:
-        out = torch.empty_like(q)
+        out = owned = torch.empty_like(q)
     else:
         _need_dense("out", out, 4)
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("out must match q's shape and dtype")
+    s = _resolve_stream(stream)
     st = lib.attn_prefill_paged(
         _dtype_code(q), _ptr(q), _ptr(k_pages), _ptr(v_pages),
         _ptr(block_table), block_table.shape[1], page_size, num_pages, code,
         _ptr(out), B, Hq, Hkv, D, Lq, int(prefix_len), float(scale),
-        _stream_handle(stream))
+        _handle(s))
     _check(st, "attn_prefill_paged")
+    _guard(s, owned)
     return out
 
 
@@ -420,8 +463,9 @@ def _topk_call(fn: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if not (q.shape == k.shape == v.shape):
         raise ValueError("q, k and v must share one shape")
     b, h, n, d = q.shape
+    owned = None
     if out is None:
-        out = torch.empty_like(q)
+        out = owned = torch.empty_like(q)
     else:
         _need_dense("out", out, 4)
         if out.shape != q.shape or out.dtype != torch.float32:
@@ -431,9 +475,11 @@ def _topk_call(fn: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         if idx_out.dtype != torch.int32 or \
                 tuple(idx_out.shape) != (b, h, n, topk):
             raise ValueError("idx_out must be int32 [b,h,n,topk]")
+    s = _resolve_stream(stream)
     st = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(idx_out),
-                          b, h, n, d, int(topk), _stream_handle(stream))
+                          b, h, n, d, int(topk), _handle(s))
     _check(st, fn)
+    _guard(s, owned)
     return out
 
 
@@ -470,15 +516,17 @@ def attn_read_probe(src: torch.Tensor, workgroups: int = 4096, *,
     if not src.is_cuda or not src.is_contiguous():
         raise ValueError("src must be a contiguous GPU tensor")
     nbytes = src.numel() * src.element_size()
+    owned = None
     if sink is None:
-        sink = torch.empty((workgroups, 4), dtype=torch.int32,
-                           device=src.device)
+        sink = owned = torch.empty((workgroups, 4), dtype=torch.int32,
+                                   device=src.device)
     elif not sink.is_contiguous() or sink.dtype != torch.int32 or \
             sink.numel() < 4 * workgroups:
         raise ValueError("sink must be contiguous int32 with >= 4*workgroups "
                          "elements")
+    s = _resolve_stream(stream)
     st = lib.attn_read_probe(_ptr(src), nbytes, _ptr(sink),
-                             sink.numel() * 4, int(workgroups),
-                             _stream_handle(stream))
+                             sink.numel() * 4, int(workgroups), _handle(s))
     _check(st, "attn_read_probe")
+    _guard(s, owned)
     return sink

@@ -16,7 +16,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int status, const char *fmt, ...) {
+attn_status fail(attn_status status, const char *fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -26,12 +26,12 @@ int fail(int status, const char *fmt, ...) {
   return status;
 }
 
-int ok() {
+attn_status ok() {
   g_last_error.clear();
   return ATTN_OK;
 }
 
-int hip_fail(hipError_t e, const char *what) {
+attn_status hip_fail(hipError_t e, const char *what) {
   return fail(ATTN_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
@@ -116,7 +116,7 @@ size_t ws_o_bytes(int B, int Hq, int S, int D) {
 
 extern "C" {
 
-const char *attn_status_str(int status) {
+const char *attn_status_str(attn_status status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK";
     case ATTN_E_ARG: return "ATTN_E_ARG: invalid argument";
@@ -150,7 +150,7 @@ namespace {
 // messages; k_new == nullptr: no append) and the launch arguments they imply;
 // split lengths are rounded up to a multiple of row_multiple. Returns ATTN_OK
 // with a.B == 0 for an empty batch (nothing to launch).
-int decode_check(const char *fn, int dtype, const void *q, const void *k_new,
+attn_status decode_check(const char *fn, attn_dtype dtype, const void *q, const void *k_new,
                  const void *v_new, const void *k_cache, const void *v_cache,
                  void *out, int B, int Hq, int Hkv, int D, int max_length,
                  int position_id, const int32_t *seq_lens, float scale,
@@ -233,7 +233,7 @@ int decode_check(const char *fn, int dtype, const void *q, const void *k_new,
   return ok();
 }
 
-int decode_impl(const char *fn, int dtype, const void *q, const void *k_new,
+attn_status decode_impl(const char *fn, attn_dtype dtype, const void *q, const void *k_new,
                 const void *v_new, const void *k_cache, const void *v_cache,
                 void *out, int B, int Hq, int Hkv, int D, int max_length,
                 int position_id, const int32_t *seq_lens, float scale,
@@ -241,7 +241,7 @@ int decode_impl(const char *fn, int dtype, const void *q, const void *k_new,
                 void *stream, const float *rope_cos = nullptr,
                 const float *rope_sin = nullptr) {
   attn::DecodeArgs a;
-  const int st = decode_check(fn, dtype, q, k_new, v_new, k_cache, v_cache,
+  const attn_status st = decode_check(fn, dtype, q, k_new, v_new, k_cache, v_cache,
                               out, B, Hq, Hkv, D, max_length, position_id,
                               seq_lens, scale, split_rows, workspace,
                               workspace_bytes, 1, a);
@@ -257,7 +257,7 @@ int decode_impl(const char *fn, int dtype, const void *q, const void *k_new,
 
 extern "C" {
 
-int attn_decode(int dtype, const void *q, const void *k_cache,
+attn_status attn_decode(attn_dtype dtype, const void *q, const void *k_cache,
                 const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
                 int max_length, int position_id, const int32_t *seq_lens,
                 float scale, int split_rows, void *workspace,
@@ -268,7 +268,7 @@ int attn_decode(int dtype, const void *q, const void *k_cache,
                      stream);
 }
 
-int attn_decode_append(int dtype, const void *q, const void *k_new,
+attn_status attn_decode_append(attn_dtype dtype, const void *q, const void *k_new,
                        const void *v_new, void *k_cache, void *v_cache,
                        void *out, int B, int Hq, int Hkv, int D, int max_length,
                        int position_id, const int32_t *seq_lens, float scale,
@@ -282,7 +282,7 @@ int attn_decode_append(int dtype, const void *q, const void *k_new,
                      stream);
 }
 
-int attn_decode_append_rope(int dtype, const void *q, const void *k_new,
+attn_status attn_decode_append_rope(attn_dtype dtype, const void *q, const void *k_new,
                             const void *v_new, const float *rope_cos,
                             const float *rope_sin, void *k_cache, void *v_cache,
                             void *out, int B, int Hq, int Hkv, int D,
@@ -302,10 +302,10 @@ int attn_decode_append_rope(int dtype, const void *q, const void *k_new,
 }
 
 
-int attn_decode_paged(int dtype, const void *q, const void *k_pages,
+attn_status attn_decode_paged(attn_dtype dtype, const void *q, const void *k_pages,
                       const void *v_pages, const int32_t *block_table,
                       int max_blocks, int page_size, int num_pages,
-                      int page_layout, void *out,
+                      attn_page_layout page_layout, void *out,
                       int B, int Hq, int Hkv, int D, int position_id,
                       const int32_t *seq_lens, float scale, int split_rows,
                       void *workspace, size_t workspace_bytes, void *stream) {
@@ -337,7 +337,7 @@ int attn_decode_paged(int dtype, const void *q, const void *k_pages,
   // [B][Hkv][max_length][D]; split lengths become multiples of the wave tile
   // so that no tile straddles a page.
   attn::DecodeArgs a;
-  const int st = decode_check(fn, dtype, q, nullptr, nullptr, k_pages, v_pages,
+  const attn_status st = decode_check(fn, dtype, q, nullptr, nullptr, k_pages, v_pages,
                               out, B, Hq, Hkv, D, max_length, position_id,
                               seq_lens, scale, split_rows, workspace,
                               workspace_bytes, tile, a);
@@ -358,7 +358,7 @@ namespace {
 
 // Checks shared by the prefill entry points; a.B == 0 on return: nothing to
 // launch.
-int prefill_check(const char *fn, int dtype, const void *q, const void *k,
+attn_status prefill_check(const char *fn, attn_dtype dtype, const void *q, const void *k,
                   const void *v, void *out, int B, int Hq, int Hkv, int D,
                   int max_length, int Lq, int prefix_len, float scale,
                   attn::PrefillArgs &a) {
@@ -405,12 +405,12 @@ int prefill_check(const char *fn, int dtype, const void *q, const void *k,
 
 extern "C" {
 
-int attn_prefill(int dtype, const void *q, const void *k_cache,
+attn_status attn_prefill(attn_dtype dtype, const void *q, const void *k_cache,
                  const void *v_cache, void *out, int B, int Hq, int Hkv, int D,
                  int max_length, int Lq, int prefix_len, float scale,
                  void *stream) {
   attn::PrefillArgs a;
-  const int st = prefill_check("attn_prefill", dtype, q, k_cache, v_cache, out,
+  const attn_status st = prefill_check("attn_prefill", dtype, q, k_cache, v_cache, out,
                                B, Hq, Hkv, D, max_length, Lq, prefix_len, scale, a);
   if (st != ATTN_OK || a.B == 0) return st;
   hipError_t e = attn::launch_prefill(a, static_cast<hipStream_t>(stream));
@@ -418,10 +418,10 @@ int attn_prefill(int dtype, const void *q, const void *k_cache,
   return ok();
 }
 
-int attn_prefill_paged(int dtype, const void *q, const void *k_pages,
+attn_status attn_prefill_paged(attn_dtype dtype, const void *q, const void *k_pages,
                        const void *v_pages, const int32_t *block_table,
                        int max_blocks, int page_size, int num_pages,
-                       int page_layout, void *out, int B, int Hq, int Hkv, int D,
+                       attn_page_layout page_layout, void *out, int B, int Hq, int Hkv, int D,
                        int Lq, int prefix_len, float scale, void *stream) {
   const char *fn = "attn_prefill_paged";
   if (page_size < 1 || max_blocks < 1 || num_pages < 1)
@@ -440,7 +440,7 @@ int attn_prefill_paged(int dtype, const void *q, const void *k_pages,
       !fits({(double)num_pages, (double)page_size, (double)Hkv, (double)D, 2.0}))
     return fail(ATTN_E_ARG, "%s: page pool extents overflow", fn);
   attn::PrefillArgs a;
-  const int st = prefill_check(fn, dtype, q, k_pages, v_pages, out, B, Hq, Hkv,
+  const attn_status st = prefill_check(fn, dtype, q, k_pages, v_pages, out, B, Hq, Hkv,
                                D, max_blocks * page_size, Lq, prefix_len, scale, a);
   if (st != ATTN_OK || a.B == 0) return st;
   if (!block_table) return fail(ATTN_E_ARG, "%s: null block_table", fn);
@@ -456,7 +456,7 @@ int attn_prefill_paged(int dtype, const void *q, const void *k_pages,
   return ok();
 }
 
-static int topk_impl(const char *fn, bool causal, const float *q, const float *k,
+static attn_status topk_impl(const char *fn, bool causal, const float *q, const float *k,
                      const float *v, float *out, int32_t *idx_out, int b, int h,
                      int n, int d, int topk, void *stream) {
   if (b < 0 || b > 65535 || h < 0 || h > 65535)
@@ -485,20 +485,20 @@ static int topk_impl(const char *fn, bool causal, const float *q, const float *k
   return ok();
 }
 
-int attn_topk(const float *q, const float *k, const float *v, float *out,
+attn_status attn_topk(const float *q, const float *k, const float *v, float *out,
               int32_t *idx_out, int b, int h, int n, int d, int topk,
               void *stream) {
   return topk_impl("attn_topk", false, q, k, v, out, idx_out, b, h, n, d, topk, stream);
 }
 
-int attn_topk_causal(const float *q, const float *k, const float *v, float *out,
+attn_status attn_topk_causal(const float *q, const float *k, const float *v, float *out,
                      int32_t *idx_out, int b, int h, int n, int d, int topk,
                      void *stream) {
   return topk_impl("attn_topk_causal", true, q, k, v, out, idx_out, b, h, n, d, topk,
                    stream);
 }
 
-int attn_read_probe(const void *src, size_t bytes, void *sink,
+attn_status attn_read_probe(const void *src, size_t bytes, void *sink,
                     size_t sink_bytes, int workgroups, void *stream) {
   const char *fn = "attn_read_probe";
   if (workgroups < 1 || workgroups > 65536)
