@@ -323,6 +323,31 @@ attn_status attn_topk_causal(const float *q, const float *k, const float *v, flo
                      int32_t *idx_out, int b, int h, int n, int d, int topk,
                      void *stream);
 
+/* Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): attn_decode with the split partials kept in a static scratch
+ * array of the library instead of a caller workspace. Arguments, result and
+ * supported set are attn_decode's, without workspace / workspace_bytes.
+ *
+ * - The library holds one scratch array of 16 MiB on every GPU it runs on,
+ *   from the first call on that GPU until the process ends; this call itself
+ *   allocates nothing.
+ * - Sizes whose split partials need more than 16 MiB
+ *   (attn_decode_workspace_bytes(B, Hq, Hkv, D, max_length, split_rows) >
+ *   16 MiB) return ATTN_E_WORKSPACE before any launch.
+ * - Every call on one GPU uses that GPU's same array: calls that may overlap
+ *   on one GPU (different streams, or host threads racing on one stream)
+ *   race on the partials and give wrong results. Serialise them. No initial
+ *   contents are needed; the array keeps the last call's contents.
+ * - The current device must be the stream's device (ATTN_E_ARG otherwise;
+ *   NULL = the null stream of the current device). */
+attn_status attn_decode_noalloc(attn_dtype dtype, const void *q,
+                                const void *k_cache, const void *v_cache,
+                                void *out, int B, int Hq, int Hkv, int D,
+                                int max_length, int position_id,
+                                const int32_t *seq_lens, float scale,
+                                int split_rows, void *stream);
+
 /* Streaming-read probe (a measurement aid, not part of the attention path):
  * reads `bytes` of device memory at src once, with 16-byte non-temporal
  * loads, to measure the read bandwidth the memory system actually delivers,

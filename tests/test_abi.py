@@ -108,6 +108,52 @@ def test_decode_batch_zero_is_a_noop():
     assert decode(B=0, ws=None, ws_bytes=0) == OK
 
 
+def decode_noalloc(**kw):
+    a = dict(dtype=BF16, q=P, k=P, v=P, out=P, B=1, Hq=32, Hkv=8, D=128,
+             max_length=8192, position_id=100, seq_lens=None, scale=0.088,
+             split_rows=0, stream=None)
+    a.update(kw)
+    return lib.attn_decode_noalloc(a["dtype"], a["q"], a["k"], a["v"], a["out"],
+                                   a["B"], a["Hq"], a["Hkv"], a["D"],
+                                   a["max_length"], a["position_id"],
+                                   a["seq_lens"], a["scale"], a["split_rows"],
+                                   a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), E_ARG),
+    (dict(Hq=24, Hkv=8), E_UNSUP),
+    (dict(D=96), E_UNSUP),
+    (dict(position_id=8192), E_ARG),
+    (dict(scale=0.0), E_ARG),
+    (dict(split_rows=-5), E_ARG),
+    (dict(out=None), E_ARG),
+    (dict(q=P + 8), E_ARG),
+    # the split partials of 64 ragged sequences at 1-row splits need far more
+    # than the 16 MiB static scratch
+    (dict(B=64, seq_lens=P, split_rows=1), E_WS),
+    (dict(B=1024, Hq=64, Hkv=8, seq_lens=P), E_WS),
+])
+def test_decode_noalloc_rejects_before_any_hip_call(kw, status):
+    assert decode_noalloc(**kw) == status
+    msg = lib.attn_last_error().decode()
+    assert msg.startswith("attn_decode_noalloc")
+    if status == E_WS:
+        assert "static scratch" in msg
+
+
+def test_decode_noalloc_scratch_limit_is_the_workspace_size():
+    # 16 MiB is the limit: the ragged B=64, Hq=32, Hkv=8, D=128 batch at
+    # max_length 8192 fits with the automatic split
+    need = lib.attn_decode_workspace_bytes(64, 32, 8, 128, 8192, 0)
+    assert 0 < need <= 16 << 20
+    assert lib.attn_decode_workspace_bytes(64, 32, 8, 128, 8192, 1) > 16 << 20
+
+
+def test_decode_noalloc_batch_zero_is_a_noop():
+    assert decode_noalloc(B=0) == OK
+
+
 def decode_append(**kw):
     a = dict(dtype=BF16, q=P, kn=P, vn=P, k=P, v=P, out=P, B=1, Hq=32, Hkv=8,
              D=128, max_length=8192, position_id=100, seq_lens=None,

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     attn_decode,
     attn_decode_append,
     attn_decode_append_rope,
+    attn_decode_noalloc,
     attn_decode_paged,
     attn_decode_workspace_bytes,
     attn_prefill,
@@ -31,7 +32,8 @@ from ._binding import (  # noqa: F401
     lib,
 )
 
-__all__ = ["attn_decode", "attn_decode_append", "attn_decode_append_rope",
+__all__ = ["attn_decode", "attn_decode_noalloc", "attn_decode_append",
+           "attn_decode_append_rope",
            "attn_decode_paged",
            "attn_prefill", "attn_prefill_paged", "attn_topk", "attn_topk_causal",
            "attn_decode_workspace_bytes", "attn_read_probe", "AttnError",

@@ -45,6 +45,9 @@ lib.attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
 lib.attn_decode.restype = _i
 lib.attn_decode.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p,
                             _f, _i, _p, _sz, _p]
+lib.attn_decode_noalloc.restype = _i
+lib.attn_decode_noalloc.argtypes = [_i, _p, _p, _p, _p, _i, _i, _i, _i, _i,
+                                    _i, _p, _f, _i, _p]
 lib.attn_decode_append.restype = _i
 lib.attn_decode_append.argtypes = [_i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i,
                                    _i, _i, _p, _f, _i, _p, _sz, _p]
@@ -69,7 +72,8 @@ lib.attn_read_probe.restype = _i
 lib.attn_read_probe.argtypes = [_p, _sz, _p, _sz, _i, _p]
 
 EXPORTED = ("attn_status_str", "attn_last_error", "attn_abi_version",
-            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_append",
+            "attn_decode_workspace_bytes", "attn_decode", "attn_decode_noalloc",
+            "attn_decode_append",
             "attn_decode_append_rope",
             "attn_decode_paged", "attn_prefill", "attn_prefill_paged",
             "attn_topk",
@@ -219,6 +223,29 @@ def attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                          _ptr(workspace), workspace.numel(), _handle(s))
     _check(st, "attn_decode")
     _guard(s, *owned)
+    return out
+
+
+def attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
+                        v_cache: torch.Tensor, out: torch.Tensor, *,
+                        position_id: Optional[int] = None,
+                        seq_lens: Optional[torch.Tensor] = None,
+                        scale: Optional[float] = None, split_rows: int = 0,
+                        stream=None) -> torch.Tensor:
+    """attn_decode with the split partials in the library's static scratch
+    (no workspace): for callers that cannot allocate. ``out`` [B,Hq,D] is
+    required. Calls that may overlap on one GPU race on the scratch."""
+    if out is None:
+        raise ValueError("attn_decode_noalloc needs out")
+    B, Hq, Hkv, D, max_length, scale, out, _, _ = _decode_args(
+        q, k_cache, v_cache, position_id, seq_lens, scale, split_rows, out,
+        torch.empty(0, dtype=torch.uint8))
+    s = _resolve_stream(stream)
+    st = lib.attn_decode_noalloc(
+        _dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B,
+        Hq, Hkv, D, max_length, -1 if position_id is None else int(position_id),
+        _ptr(seq_lens), scale, int(split_rows), _handle(s))
+    _check(st, "attn_decode_noalloc")
     return out
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/attn.h"
@@ -266,6 +267,77 @@ attn_status attn_decode(attn_dtype dtype, const void *q, const void *k_cache,
                      v_cache, out, B, Hq, Hkv, D, max_length, position_id,
                      seq_lens, scale, split_rows, workspace, workspace_bytes,
                      stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode: the split partials live in a file-scope device
+// array instead of a caller workspace. Each GPU the library runs on holds its
+// own copy of the array (kScratchBytes) until the process ends. In host code
+// the array's name is not a device address: the address of each GPU's copy
+// is looked up once, with that GPU current, and only that address is passed
+// to the kernels.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+void *g_scratch_dev[kMaxDevices];  // device address of scratch, per GPU
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+extern "C" {
+
+attn_status attn_decode_noalloc(attn_dtype dtype, const void *q,
+                                const void *k_cache, const void *v_cache,
+                                void *out, int B, int Hq, int Hkv, int D,
+                                int max_length, int position_id,
+                                const int32_t *seq_lens, float scale,
+                                int split_rows, void *stream) {
+  const char *fn = "attn_decode_noalloc";
+  // Every argument check first, on host scalars: a stand-in workspace
+  // address (never dereferenced) and the scratch size.
+  {
+    attn::DecodeArgs probe;
+    const size_t need = attn_decode_workspace_bytes(
+        B, Hq, Hkv, D, max_length, split_rows < 0 ? 0 : split_rows);
+    if (need > kScratchBytes)
+      return fail(ATTN_E_WORKSPACE,
+                  "%s: these sizes need %zu bytes of split scratch, the static "
+                  "scratch holds %zu (use attn_decode with a workspace)",
+                  fn, need, kScratchBytes);
+    const attn_status st = decode_check(
+        fn, dtype, q, nullptr, nullptr, k_cache, v_cache, out, B, Hq, Hkv, D,
+        max_length, position_id, seq_lens, scale, split_rows,
+        reinterpret_cast<void *>(uintptr_t(256)), kScratchBytes, 1, probe);
+    if (st != ATTN_OK || probe.B == 0) return st;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_E_UNSUPPORTED, "%s: device %d >= %d", fn, dev, kMaxDevices);
+  if (stream != nullptr) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return hip_fail(e, fn);
+    if (sdev != dev)
+      return fail(ATTN_E_ARG, "%s: stream belongs to device %d, device %d is current",
+                  fn, (int)sdev, dev);
+  }
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void *p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_dev[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess)
+    return hip_fail(g_scratch_err[dev], "attn_decode_noalloc: scratch address");
+  return decode_impl(fn, dtype, q, nullptr, nullptr, k_cache, v_cache, out, B,
+                     Hq, Hkv, D, max_length, position_id, seq_lens, scale,
+                     split_rows, g_scratch_dev[dev], kScratchBytes, stream);
 }
 
 attn_status attn_decode_append(attn_dtype dtype, const void *q, const void *k_new,
