@@ -36,6 +36,7 @@ import hashlib
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -59,8 +60,6 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="approximate oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the single-sequence position-8000 figures")
@@ -469,56 +468,126 @@ def bench_read_probe(torch, tas, gib=4, reps=20):
                 GBps_by_workgroups=by_wg)
 
 
-def cpu_baseline(dec, synth, budget_s):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(dec, synth):
+    """The fp64 NumPy oracle, as it stands, timed on this machine's host
+    cores on a bounded sample of every configuration point: one warm-up run
+    and the median of three, once with as many BLAS threads as the process
+    may use and once with one, reported in the numerators of the GPU line
+    (decode bytes per second, prefill and top-k FLOP per second). Inputs are
+    generated and converted to float before the timed runs."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()]
-                      or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    p = dec["p"]
-    lens = dec["lens"]
-    done, nbytes, t_total = 0, 0, 0.0
-    gpu_out = dec["out"].float().cpu().numpy().astype(np.float64)
-    max_err = 0.0
-    for b in range(p["B"]):
-        L = int(lens[b])
-        qb, kb, vb = synth.ragged_sequence(p["seed"], b, p["Hq"], p["Hkv"],
-                                           p["D"], L, "bf16")
-        qf, kf, vf = (synth.bf16_to_f32(x) for x in (qb, kb, vb))
-        t0 = time.perf_counter()
-        ref = oracle.decode_sequence(qf, kf, vf, L, p["scale"])
-        t_total += time.perf_counter() - t0
-        max_err = max(max_err, float(np.max(np.abs(ref - gpu_out[b]))))
-        nbytes += 2 * p["Hkv"] * p["D"] * 2 * L + 2 * p["Hq"] * p["D"] * 2
-        done += 1
-        if t_total >= budget_s:
-            break
-    # the same oracle on one BLAS thread, over the first sequence
-    single = None
-    try:
-        from threadpoolctl import threadpool_limits
-        L = int(lens[0])
-        qb, kb, vb = synth.ragged_sequence(p["seed"], 0, p["Hq"], p["Hkv"],
-                                           p["D"], L, "bf16")
-        qf, kf, vf = (synth.bf16_to_f32(x) for x in (qb, kb, vb))
-        with threadpool_limits(limits=1):
+    from threadpoolctl import threadpool_limits
+
+    W = synth.WORKLOADS
+    f32 = synth.as_f32
+    points = []  # (name, fn, numerator, unit, sample)
+
+    p1 = W["decode_f32_tiny"].params
+    c1 = synth.decode_uniform(p1["seed"], p1["B"], p1["Hq"], p1["Hkv"], p1["D"],
+                              p1["max_length"], p1["position_id"], "f32",
+                              poison=True, scale=p1["scale"])
+    nb1 = 2 * p1["Hkv"] * p1["D"] * 4 * (p1["position_id"] + 1) + \
+        2 * p1["Hq"] * p1["D"] * 4
+    points.append(("decode_f32_tiny", lambda: oracle.decode(
+        c1.q, c1.k_cache, c1.v_cache, position_id=p1["position_id"],
+        scale=p1["scale"]), nb1, "GB/s", "whole workload"))
+
+    p2 = W["decode_gqa_static"].params
+    c2 = synth.decode_uniform(p2["seed"], p2["B"], p2["Hq"], p2["Hkv"], p2["D"],
+                              p2["max_length"], p2["max_length"] - 1, "bf16",
+                              poison=False, scale=p2["scale"])
+    q2, k2, v2 = (f32(x, "bf16") for x in (c2.q, c2.k_cache, c2.v_cache))
+    for pos in p2["positions"]:
+        nb = 2 * p2["Hkv"] * p2["D"] * 2 * (pos + 1) + 2 * p2["Hq"] * p2["D"] * 2
+        points.append((f"decode_gqa_static_p{pos}", lambda pos=pos: oracle.decode(
+            q2, k2, v2, position_id=pos, scale=p2["scale"]), nb, "GB/s",
+            "whole workload"))
+
+    p3 = dec["p"]
+    n3 = p3["B"]
+    seqs = []
+    nb3 = 0
+    for b in range(n3):
+        L = int(dec["lens"][b])
+        qb, kb, vb = synth.ragged_sequence(p3["seed"], b, p3["Hq"], p3["Hkv"],
+                                           p3["D"], L, "bf16")
+        seqs.append((L,) + tuple(synth.bf16_to_f32(x) for x in (qb, kb, vb)))
+        nb3 += 2 * p3["Hkv"] * p3["D"] * 2 * L + 2 * p3["Hq"] * p3["D"] * 2
+    outs3 = []
+
+    def run3():
+        outs3.clear()
+        for L, qf, kf, vf in seqs:
+            outs3.append(oracle.decode_sequence(qf, kf, vf, L, p3["scale"]))
+    points.append(("decode_ragged_b64", run3, nb3, "GB/s",
+                   f"all {n3} sequences ({sum(x[0] for x in seqs)} rows)"))
+
+    p4 = W["prefill_prefix3072"].params
+    c4 = synth.prefill(p4["seed"], p4["B"], p4["Hq"], p4["Hkv"], p4["D"],
+                       p4["Lq"], p4["prefix_len"], p4["max_length"], "bf16",
+                       scale=p4["scale"])
+    h4 = p4["Hq"]
+    q4, k4, v4 = (np.ascontiguousarray(f32(x, "bf16")[:, :h4])
+                  for x in (c4.q, c4.k_cache, c4.v_cache))
+    fl4 = 4 * p4["D"] * h4 * sum(p4["prefix_len"] + i + 1 for i in range(p4["Lq"]))
+    points.append(("prefill_prefix3072", lambda: oracle.prefill(
+        q4, k4, v4, p4["prefix_len"], scale=p4["scale"]), fl4, "GFLOP/s",
+        f"all {h4} heads"))
+
+    p5 = W["topk_c2psa"].params
+    c5 = synth.topk(p5["seed"], p5["b"], p5["h"], p5["n"], p5["d"], p5["topk"])
+    b5 = 8
+    q5, k5, v5 = (np.ascontiguousarray(x[:b5]) for x in (c5.q, c5.k, c5.v))
+    fl5 = b5 * p5["h"] * p5["n"] * (2 * p5["n"] * p5["d"] + 2 * p5["topk"] * p5["d"])
+    points.append(("topk_c2psa", lambda: oracle.topk_sparse(
+        q5, k5, v5, p5["topk"]), fl5, "GFLOP/s",
+        f"batches 0-{b5 - 1} of {p5['b']} ({b5 * p5['h']} of {p5['b'] * p5['h']} (b, h))"))
+
+    def median3(fn):
+        fn()  # warm-up
+        ts = []
+        for _ in range(3):
             t0 = time.perf_counter()
-            oracle.decode_sequence(qf, kf, vf, L, p["scale"])
-            t1 = time.perf_counter() - t0
-        nb1 = 2 * p["Hkv"] * p["D"] * 2 * L + 2 * p["Hq"] * p["D"] * 2
-        single = dict(value=round(nb1 / t1 / 1e9, 4), unit="GB/s", cores=1,
-                      sample=f"sequence 0 ({L} rows, {nb1} bytes) in {t1:.2f} s")
-    except Exception as exc:  # pragma: no cover
-        single = dict(error=str(exc))
-    return dict(value=round(nbytes / t_total / 1e9, 4), unit="GB/s",
-                cores=int(threads), kind="oracle", single_thread=single,
-                sample=(f"fp64 NumPy oracle over the first {done} of 64 "
-                        f"sequences of the ragged decode batch "
-                        f"({nbytes} algorithmic bytes in {t_total:.2f} s)"),
-                spot_check_max_abs_err=max_err)
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    cores = len(os.sched_getaffinity(0))
+    res = {}
+    t_start = time.perf_counter()
+    for threads in (cores, 1):
+        key = "all_cores" if threads == cores else "one_thread"
+        with threadpool_limits(limits=threads):
+            for name, fn, num, unit, sample in points:
+                sec = median3(fn)
+                r = res.setdefault(name, {"unit": unit, "sample": sample,
+                                          "numerator": num})
+                r[key] = {"s": round(sec, 6), "rate": round(num / sec / 1e9, 4)}
+    wall = time.perf_counter() - t_start
+    # spot check of the GPU's ragged-batch output against the sampled oracle
+    gpu_out = dec["out"].float().cpu().numpy().astype(np.float64)
+    err = max(float(np.max(np.abs(o - gpu_out[b]))) for b, o in enumerate(outs3))
+    head = res["decode_ragged_b64"]
+    return dict(value=head["all_cores"]["rate"], unit="GB/s", cores=cores,
+                kind="oracle",
+                sample=(f"fp64 NumPy oracle on the ragged decode batch "
+                        f"({head['sample']}, {head['numerator']} algorithmic "
+                        "bytes); median of 3 after 1 warm-up"),
+                one_thread=head["one_thread"]["rate"], cpu_model=cpu_model(),
+                threads={"all_cores": cores, "one_thread": 1},
+                points=res, wall_s=round(wall, 1),
+                spot_check_max_abs_err=err)
 
 
 # ----------------------------------------------------------------------------
@@ -710,7 +779,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(dec, synth, args.cpu_seconds)
+        cpu = cpu_baseline(dec, synth)
 
     line = {
         "metric": METRIC,
