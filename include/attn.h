@@ -59,7 +59,16 @@
 extern "C" {
 #endif
 
-typedef enum attn_status {
+/* The enums below are int-sized. In C++ their underlying type is fixed to
+ * int, so that any int a caller passes (an unknown dtype, for instance, which
+ * the library rejects with ATTN_E_ARG) is a valid value of the parameter. */
+#ifdef __cplusplus
+#define ATTN_ENUM_BASE : int
+#else
+#define ATTN_ENUM_BASE
+#endif
+
+typedef enum attn_status ATTN_ENUM_BASE {
   ATTN_OK = 0,
   ATTN_E_ARG = 1,         /* invalid argument (null pointer, bad size, ...) */
   ATTN_E_UNSUPPORTED = 2, /* valid, but outside the supported set          */
@@ -67,7 +76,7 @@ typedef enum attn_status {
   ATTN_E_HIP = 4          /* a HIP launch or runtime call failed           */
 } attn_status;
 
-typedef enum attn_dtype {
+typedef enum attn_dtype ATTN_ENUM_BASE {
   ATTN_F32 = 0,  /* IEEE binary32                                          */
   ATTN_BF16 = 1  /* bfloat16 (upper 16 bits of binary32)                    */
 } attn_dtype;
@@ -188,7 +197,7 @@ attn_status attn_decode_append_rope(attn_dtype dtype, const void *q, const void 
                             void *stream);
 
 /* Page layouts of attn_decode_paged and attn_prefill_paged. */
-typedef enum attn_page_layout {
+typedef enum attn_page_layout ATTN_ENUM_BASE {
   ATTN_PAGES_TOKEN_MAJOR = 0, /* page [page_size][Hkv][D]                  */
   ATTN_PAGES_HEAD_MAJOR = 1   /* page [Hkv][page_size][D]                  */
 } attn_page_layout;

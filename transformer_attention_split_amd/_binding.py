@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libattn.so")
+# ATTN_LIB_PATH selects another build of the same library (the host-sanitized
+# test build of the C ABI layer); by default the in-tree libattn.so.
+LIB_PATH = os.environ.get("ATTN_LIB_PATH") or os.path.join(_PKG, "libattn.so")
 
 ATTN_OK, ATTN_E_ARG, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = range(5)
 ATTN_F32, ATTN_BF16 = 0, 1

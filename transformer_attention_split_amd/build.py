@@ -3,7 +3,9 @@
 Every source is compiled on each call (objects go to ``_build/`` at the
 repository root) and linked into ``transformer_attention_split_amd/libattn.so``.
 Run as ``python transformer_attention_split_amd/build.py`` (by path, so that
-the package, which loads the library on import, is not imported first).
+the package, which loads the library on import, is not imported first);
+``--sanitize`` builds the host-sanitized test library of the C ABI layer
+instead (``_build/san/libattn_san.so``).
 """
 from __future__ import annotations
 
@@ -82,5 +84,64 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+# Host-side sanitizers for the C ABI layer (argument checks, planning,
+# error reporting): api.cpp is compiled with AddressSanitizer and
+# UndefinedBehaviorSanitizer on its host pass only (each -fsanitize= follows
+# -Xarch_host; the device code is built as usual) and linked with the normal
+# kernel objects into a separate test library. Loading it needs the ASan
+# runtime preloaded (asan_runtime()).
+SAN_DIR = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libattn_san.so")
+SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address",
+                  "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all",
+                  "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The shared ASan runtime of the HIP toolchain's clang."""
+    hipcc = os.path.realpath(_hipcc())
+    roots = [os.path.join(os.path.dirname(os.path.dirname(hipcc)), "llvm"),
+             "/opt/rocm/llvm"]
+    for root in roots:
+        base = os.path.join(root, "lib", "clang")
+        if not os.path.isdir(base):
+            continue
+        for ver in sorted(os.listdir(base), reverse=True):
+            cand = os.path.join(base, ver, "lib", "linux",
+                                "libclang_rt.asan-x86_64.so")
+            if os.path.exists(cand):
+                return cand
+    raise RuntimeError("libclang_rt.asan-x86_64.so not found")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Build SAN_LIB: api.cpp with host ASan + UBSan, kernels as in build()."""
+    build(verbose=verbose)  # kernel objects in BUILD
+    hipcc = _hipcc()
+    os.makedirs(SAN_DIR, exist_ok=True)
+    api_o = os.path.join(SAN_DIR, "api.o")
+    cmd = [hipcc, *HIPFLAGS, "-O1", "-g", *SAN_HOST_FLAGS, "-x", "hip", "-c",
+           os.path.join(CSRC, "api.cpp"), "-o", api_o]
+    rc, out = _run(cmd)
+    if verbose or rc != 0:
+        print(out, file=sys.stderr)
+    if rc != 0:
+        raise RuntimeError(f"hipcc failed ({rc}): {' '.join(cmd)}")
+    objs = [api_o] + [os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+                      for src in SOURCES if src != "api.cpp"]
+    rc, out = _run([hipcc, f"--offload-arch={ARCH}", "-shared",
+                    "-Xarch_host", "-fsanitize=address",
+                    "-Xarch_host", "-fsanitize=undefined", "-shared-libsan",
+                    "-o", SAN_LIB, *objs])
+    if rc != 0:
+        print(out, file=sys.stderr)
+        raise RuntimeError("link of the sanitized library failed")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -61,6 +61,7 @@ bool fits(std::initializer_list<double> dims) {
 // pay more per-workgroup start-up and combine work).
 // ---------------------------------------------------------------------------
 constexpr long kTargetBlocks = 5120;
+constexpr long kCUs = 256;  // compute units of an MI355X
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
@@ -88,6 +89,13 @@ attn::DecodePlan plan_decode(int B, int Hkv, int D, int max_length,
     const int q = row_quantum(D);
     int sr = ceil_div(L_bound, auto_split_target(B, Hkv));
     sr = ceil_div(sr, q) * q;
+    // One round of the four wave tiles per workgroup only while the grid
+    // fits one workgroup per CU; past that, two rounds. Measured on one
+    // sequence (8 kv heads, D 128, graph replay, cold cache): at position
+    // 8000, 504 one-round workgroups 14.2 us against 252 two-round ones
+    // 12.9 us; at position 4000, 256 one-round workgroups 10.6 us against
+    // 11.8 us.
+    if (sr == q && (long)B * Hkv * ceil_div(L_bound, q) > kCUs) sr = 2 * q;
     p.split_rows = effective_split_rows(max_length, sr);
   }
   p.splits = ceil_div(L_bound, p.split_rows);
