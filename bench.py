@@ -315,11 +315,13 @@ def bench_paged(torch, tas, dec, steps, page_size, layout):
 # ----------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the decode workload
 # ----------------------------------------------------------------------------
-def bench_prefill_shape(torch, tas, synth, D, H, n=20):
-    """The prefill workload's prefix and new tokens with head size D and H
-    heads, n back-to-back calls between two events."""
+def bench_prefill_shape(torch, tas, synth, D, H, n=20, Hkv=None):
+    """The prefill workload's prefix and new tokens with head size D, H query
+    heads over Hkv kv heads (default H), n back-to-back calls between two
+    events."""
     p = synth.WORKLOADS["prefill_prefix3072"].params
-    inp = synth.prefill(p["seed"], 1, H, H, D, p["Lq"], p["prefix_len"],
+    Hkv = H if Hkv is None else Hkv
+    inp = synth.prefill(p["seed"], 1, H, Hkv, D, p["Lq"], p["prefix_len"],
                         p["max_length"], "bf16", poison=False, scale=D ** -0.5)
     q, k, v = (bf16_dev(x, torch) for x in (inp.q, inp.k_cache, inp.v_cache))
     out = torch.empty_like(q)
@@ -341,7 +343,8 @@ def bench_prefill_shape(torch, tas, synth, D, H, n=20):
     flops = 4 * D * H * sum(p["prefix_len"] + i + 1 for i in range(p["Lq"]))
     del q, k, v, out
     torch.cuda.empty_cache()
-    return dict(workload=f"prefill_prefix3072 at D={D} ({H} heads)",
+    return dict(workload=f"prefill_prefix3072 at D={D} ({H} query heads over "
+                         f"{Hkv} kv heads)",
                 us_back_to_back=round(us, 2), flops=flops,
                 TFLOPs_back_to_back=round(flops / us / 1e6, 1),
                 frac_of_bf16_mfma_peak=round(flops / us / 1e6
@@ -745,11 +748,13 @@ def main():
         secondary["decode_paged_ragged_b64"] = [
             bench_paged(torch, tas, dec, args.steps, ps, lay)
             for lay in ("token", "head") for ps in (64, 256)]
-        log("prefill at D=128 and with 32 heads ...")
+        log("prefill at D=128 (16 heads; 32 over 8 kv heads) and with 32 heads ...")
         secondary["prefill_d128_prefix3072"] = bench_prefill_shape(
             torch, tas, synth, 128, 16)
         secondary["prefill_h32_prefix3072"] = bench_prefill_shape(
             torch, tas, synth, 64, 32)
+        secondary["prefill_d128_gqa32x8_prefix3072"] = bench_prefill_shape(
+            torch, tas, synth, 128, 32, Hkv=8)
         log("paged prefill ...")
         secondary["prefill_paged_prefix3072"] = [
             bench_prefill_paged(torch, tas, pre, ps, lay)
