@@ -14,7 +14,11 @@ Recipe (the same for tests and the benchmark):
   when ``poison`` is set, so a kernel that reads them produces NaN;
 * ragged batches draw the lengths first from ``default_rng(seed)`` and then
   every sequence from its own ``default_rng([seed, b])`` so one sequence can
-  be regenerated without the others.
+  be regenerated without the others;
+* "needle" inputs (``plant_needles``) overwrite a few keys of each
+  sequence and kv head after the draw with one key that the head's query
+  group scores far above the rest, so that those rows carry nearly all the
+  attention weight and the output stays of order one at any length.
 
 bf16 tensors are returned as ``uint16`` bit patterns; ``bf16_to_f32`` gives
 their exact float32 values.
@@ -152,6 +156,50 @@ def iter_ragged(seed: int, B: int, Hq: int, Hkv: int, D: int,
     for b in range(B):
         L = int(min(max(int(lengths[b]), 0), max_length))
         yield (b, L) + ragged_sequence(seed, b, Hq, Hkv, D, L, dtype)
+
+
+def plant_needles(seed: int, q: np.ndarray, k_cache: np.ndarray,
+                  lengths: np.ndarray, dtype: str, n_rows: int = 3,
+                  margin: float = 8.0) -> np.ndarray:
+    """Overwrite keys of a drawn decode batch (in place) with needles.
+
+    q [B, Hq, D] and k_cache [B, Hkv, M, D] as stored; query heads
+    g*G .. g*G+G-1 share kv head g (G = Hq / Hkv). For every sequence b of
+    length L > 0 (lengths clamped to [0, M]) and kv head g, let u be the unit
+    vector along the sum of the group's queries and m the smallest product
+    q_h . u over the group; the needle key is alpha * u with alpha chosen so
+    that m * alpha / sqrt(D) = log(L) + margin. Against L keys whose scaled
+    products are about N(0, 1) the needles then hold all but about
+    e^(0.5 - margin) of the weight. The rows overwritten are min(n_rows, L)
+    distinct valid rows drawn from ``default_rng([seed, 11])`` plus row 0
+    (even g) or row L - 1 (odd g). Returns the needle keys [B, Hkv, D] as
+    stored (zero for empty sequences)."""
+    B, Hq, D = q.shape
+    Hkv, M = k_cache.shape[1], k_cache.shape[2]
+    G = Hq // Hkv
+    qf = as_f32(q, dtype).astype(np.float64)
+    rng = np.random.default_rng([seed, 11])
+    keys = np.zeros((B, Hkv, D), k_cache.dtype)
+    for b in range(B):
+        L = int(min(max(int(lengths[b]), 0), M))
+        if L == 0:
+            continue
+        for g in range(Hkv):
+            grp = qf[b, g * G:(g + 1) * G]
+            u = grp.sum(0)
+            u /= np.linalg.norm(u)
+            m = float((grp @ u).min())
+            if m <= 1.0:
+                raise ValueError(f"query group ({b}, {g}) has no common direction")
+            alpha = (np.log(L) + margin) * np.sqrt(D) / m
+            key = (alpha * u).astype(np.float32)
+            enc = f32_to_bf16_bits(key) if dtype == "bf16" else key
+            rows = set(rng.choice(L, size=min(n_rows, L), replace=False).tolist())
+            rows.add(0 if g % 2 == 0 else L - 1)
+            keys[b, g] = enc
+            for r in rows:
+                k_cache[b, g, r] = enc
+    return keys
 
 
 def new_token_kv(seed: int, B: int, Hkv: int, D: int, dtype: str):

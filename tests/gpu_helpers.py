@@ -1,4 +1,5 @@
-"""Shared helpers for the GPU parity tests (host <-> device plumbing only)."""
+"""Shared helpers for the GPU parity tests (host <-> device plumbing and the
+error checks)."""
 import sys
 
 import numpy as np
@@ -36,3 +37,10 @@ def max_abs_err(a: np.ndarray, b: np.ndarray) -> float:
     assert a.shape == b.shape, (a.shape, b.shape)
     assert np.all(np.isfinite(a)), "non-finite values in the GPU result"
     return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def assert_discriminating(ref: np.ndarray, dtype: str) -> None:
+    """The expected output is far from zero against the tolerance, so that a
+    result that skipped rows or tiles cannot pass by being near zero."""
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    assert rms > 10 * tol(dtype), rms

@@ -5,7 +5,8 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import max_abs_err, say, to_dev, to_host64, tol
+from gpu_helpers import (assert_discriminating, max_abs_err, say, to_dev,
+                         to_host64, tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,6 +107,55 @@ def test_decode_ragged_batch64_full():
     out = tas.attn_decode(q, k, v, seq_lens=sl, scale=p["scale"])
     torch.cuda.synchronize()
     err = max_abs_err(to_host64(out), np.stack(refs))
+    assert err <= tol("bf16"), err
+
+
+def test_decode_ragged_batch64_full_needles():
+    # The same workload with needle keys: over thousands of random keys the
+    # output shrinks to about the bf16 tolerance, while needles keep it of
+    # order one, so a split or tile that is skipped or read at the wrong rows
+    # shows up.
+    p = synth.WORKLOADS["decode_ragged_b64"].params
+    B, Hq, Hkv, D, M = p["B"], p["Hq"], p["Hkv"], p["D"], p["max_length"]
+    lens = synth.ragged_lengths(p["seed"], B, M)
+    q = torch.empty(B, Hq, D, dtype=torch.bfloat16, device="cuda")
+    k = torch.full((B, Hkv, M, D), float("nan"), dtype=torch.bfloat16,
+                   device="cuda")
+    v = torch.full_like(k, float("nan"))
+    refs = []
+    for b, L, qb, kb, vb in synth.iter_ragged(p["seed"], B, Hq, Hkv, D, M,
+                                               "bf16", lens):
+        synth.plant_needles(p["seed"] + b, qb[None], kb[None],
+                            np.array([L]), "bf16", n_rows=4)
+        q[b] = to_dev(qb, "bf16")
+        k[b, :, :L] = to_dev(kb, "bf16")
+        v[b, :, :L] = to_dev(vb, "bf16")
+        refs.append(oracle.decode_sequence(synth.as_f32(qb, "bf16"),
+                                           synth.as_f32(kb, "bf16"),
+                                           synth.as_f32(vb, "bf16"), L,
+                                           p["scale"]))
+    ref = np.stack(refs)
+    assert_discriminating(ref, "bf16")
+    sl = torch.from_numpy(lens).cuda()
+    say(f"decode bf16 ragged B=64 needles sum(L)={int(lens.sum())}")
+    out = tas.attn_decode(q, k, v, seq_lens=sl, scale=p["scale"])
+    torch.cuda.synchronize()
+    err = max_abs_err(to_host64(out), ref)
+    assert err <= tol("bf16"), err
+
+
+@pytest.mark.parametrize("pos", [1000, 8000])
+def test_decode_gqa_static_needles(pos):
+    p = synth.WORKLOADS["decode_gqa_static"].params
+    inp = synth.decode_uniform(p["seed"], p["B"], p["Hq"], p["Hkv"], p["D"],
+                               p["max_length"], pos, "bf16", poison=True,
+                               scale=p["scale"])
+    synth.plant_needles(p["seed"], inp.q, inp.k_cache,
+                        np.full(p["B"], pos + 1), "bf16")
+    ref = oracle_of(inp)
+    assert_discriminating(ref, "bf16")
+    say(f"decode bf16 static position={pos} needles")
+    err = max_abs_err(to_host64(run_decode(inp)), ref)
     assert err <= tol("bf16"), err
 
 
