@@ -3,6 +3,7 @@
 // Every check below runs on host scalars before any HIP call, so an invalid
 // call never touches the device. Nothing here allocates device memory or
 // synchronises a stream.
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -103,6 +104,63 @@ attn::DecodePlan plan_decode(int B, int Hkv, int D, int max_length,
   return p;
 }
 
+// Balanced schedule (ragged bf16 batches of at most kBalancedMaxB sequences;
+// the device side is described in decode.hip): P = two workgroups per CU,
+// the split kernel's occupancy, so that every workgroup of the launch is
+// resident and streams from start to end (fewer when the batch at full
+// length holds fewer ranges of C_min tiles); each takes at least C_min wave
+// tiles. Workgroup i takes range (i % 8) * (P / 8) + i / 8, so that each
+// XCD streams a contiguous run of ranges (160.9 against 161.9 us on the
+// ragged batch below, 167.5 against 172.4 us with its sequences sorted by
+// length). Forcing split_rows sets C_min = ceil(split_rows / tile); otherwise
+// C_min is two rounds of the four wave tiles (one round while the whole
+// batch at full length fits one round per CU) or an eighth of a
+// workgroup's share of the batch at full length, whichever is larger, so
+// that batches of shorter sequences still occupy the grid. C_min is at least
+// ceil(n_max / (kDecodeMaxSplits - 1)), which bounds the pieces of one
+// (b, kv head) by S = ceil(n_max / C_min) + 1 <= kDecodeMaxSplits (n_max:
+// wave tiles of max_length rows). Measured per call (split and combine) on
+// 64 uniformly ragged sequences of up to 8192 rows (Hkv 8, D 128): 160.9 us
+// against 171.1 us with one 896-row split per workgroup, whose launch ended
+// in a tail of the longest sequences' last splits; 64 sequences of 4096
+// rows: 162.3 against 176.8 us.
+struct BalancedPlan {
+  bool ok;
+  int P, C_min, S;
+};
+
+BalancedPlan plan_balanced(int B, int Hkv, int D, int max_length,
+                           int split_rows) {
+  BalancedPlan p{};
+  const long tile = 4096 / D;
+  const long n_max = ceil_div(max_length, tile);
+  const long tt_max = (long)B * Hkv * n_max;
+  p.P = 2 * (int)kCUs;
+  // (one sequence has nothing to balance: its equal splits of the plain
+  // grid finish together, while a range that straddles two kv heads runs
+  // two pieces in turn: 13.3 against 15.7 us at 8001 rows, Hkv 8, D 128)
+  if (B < 2 || B > attn::kBalancedMaxB || tt_max + p.P > INT_MAX) return p;
+  long cmin;
+  if (split_rows > 0) {
+    cmin = ceil_div(split_rows, tile);
+  } else {
+    cmin = tt_max / 4 > kCUs ? 8 : 4;
+    const long share = ceil_div(tt_max, 8L * p.P);
+    if (share > cmin) cmin = share;
+  }
+  const long floor_tiles = ceil_div(n_max, attn::kDecodeMaxSplits - 1);
+  if (cmin < floor_tiles) cmin = floor_tiles;
+  if (cmin > INT_MAX / p.P) cmin = INT_MAX / p.P;
+  p.C_min = (int)cmin;
+  // no more workgroups than ranges of C_min tiles in the batch at full
+  // length (a multiple of 8, the XCD count)
+  const long need = (ceil_div(tt_max, cmin) + 7) / 8 * 8;
+  if (need < p.P) p.P = (int)need;
+  p.S = ceil_div(n_max, cmin) + 1;
+  p.ok = true;
+  return p;
+}
+
 // Upper bound on splits for any valid length <= max_length.
 int max_splits(int B, int Hkv, int D, int max_length, int split_rows) {
   if (split_rows > 0)
@@ -147,7 +205,11 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D,
   if (B == 0) return 0;
   if (!fits({(double)B, (double)Hq, (double)max_length, (double)D}))
     return 0;
-  const int S = max_splits(B, Hkv, D, max_length, split_rows);
+  // a bound for both schedules (the balanced one is taken for ragged bf16
+  // batches)
+  int S = max_splits(B, Hkv, D, max_length, split_rows);
+  const BalancedPlan bp = plan_balanced(B, Hkv, D, max_length, split_rows);
+  if (bp.ok && bp.S > S) S = bp.S;
   return ws_ml_bytes(B, Hq, S) + ws_o_bytes(B, Hq, S, D);
 }
 
@@ -225,7 +287,16 @@ attn_status decode_check(const char *fn, attn_dtype dtype, const void *q, const 
   a.seq_lens = seq_lens;
   a.scale = scale;
   a.plan = plan_decode(B, Hkv, D, max_length, L_bound, split_rows);
-  if (a.plan.split_rows % row_multiple != 0) {  // fewer splits: still fits
+  if (seq_lens && dtype == ATTN_BF16) {
+    const BalancedPlan bp = plan_balanced(B, Hkv, D, max_length, split_rows);
+    if (bp.ok) {
+      a.plan.balanced = 1;
+      a.plan.P = bp.P;
+      a.plan.C_min = bp.C_min;
+      a.plan.splits = bp.S;  // pieces start at wave-tile rows: no page straddles
+    }
+  }
+  if (!a.plan.balanced && a.plan.split_rows % row_multiple != 0) {  // fewer splits: still fits
     a.plan.split_rows = ceil_div(a.plan.split_rows, row_multiple) * row_multiple;
     a.plan.splits = ceil_div(L_bound, a.plan.split_rows);
   }

@@ -65,4 +65,18 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes: DPP row shifts inside each
+// 16-lane row (out-of-row sources contribute 0), then the totals of the
+// earlier rows read with readlane.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, int lane) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);
+  const uint32_t t0 = __builtin_amdgcn_readlane(x, 15);
+  const uint32_t t1 = __builtin_amdgcn_readlane(x, 31);
+  const uint32_t t2 = __builtin_amdgcn_readlane(x, 47);
+  return x + (lane >= 16 ? t0 : 0u) + (lane >= 32 ? t1 : 0u) + (lane >= 48 ? t2 : 0u);
+}
+
 }  // namespace attn

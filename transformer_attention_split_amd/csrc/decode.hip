@@ -135,12 +135,7 @@ struct Unit {
 };
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  return x;
+  return (int)wave_inclusive_scan((uint32_t)x, lane);  // (counts are >= 0)
 }
 
 // The work unit of this workgroup (the orders are described at the top).
@@ -185,6 +180,65 @@ __device__ __forceinline__ Unit locate_unit(const int32_t *seq_lens, int B,
   return u;
 }
 
+// ---------------------------------------------------------------------------
+// Balanced schedule (bf16, per-sequence lengths, B <= kBalancedMaxB)
+// ---------------------------------------------------------------------------
+// The work of the batch is the list of wave tiles (BN rows) of every
+// (sequence b, kv head g) in the order (b, g, tile): n_b = ceil(L_b / BN)
+// tiles per kv head of sequence b, TT = Hkv * sum_b n_b in all. Workgroup w
+// of the P launched takes the tiles [w*C, (w+1)*C), C = max(C_min,
+// ceil(TT / P)), so every workgroup streams the same number of rows (to
+// within one tile per piece) whatever the lengths, and a long sequence no
+// longer ends the launch alone. A range cuts one or more (b, g) into pieces.
+// A (b, g) inside one range is finished there; the others leave one partial
+// per piece, in slot w - first(b, g), first(b, g) = floor(start(b, g) / C),
+// start(b, g) = Hkv * P_b + g * n_b (P_b: the tiles of the sequences before
+// b), which the combine kernel finds from the same lengths.
+__device__ __forceinline__ int clamp_len(int L, int max_length) {
+  return L < 0 ? 0 : (L > max_length ? max_length : L);
+}
+
+struct BatchTiles {
+  int len[kBalancedMaxB / 64];   // clamped length of sequence 64c + lane
+  int cnt[kBalancedMaxB / 64];   // n_b of sequence 64c + lane
+  int incl[kBalancedMaxB / 64];  // sum of n_b' over b' <= 64c + lane
+  int total;                     // sum of n_b over the batch (wave-uniform)
+};
+
+__device__ __forceinline__ BatchTiles batch_tiles(const int32_t *seq_lens,
+                                                  int B, int max_length,
+                                                  int BN) {
+  const int lane = threadIdx.x % 64;
+  BatchTiles t;
+  t.total = 0;
+#pragma unroll
+  for (int c = 0; c < kBalancedMaxB / 64; ++c) {
+    const int bi = 64 * c + lane;
+    t.len[c] = bi < B ? clamp_len(seq_lens[bi], max_length) : 0;
+    t.cnt[c] = (t.len[c] + BN - 1) / BN;
+    t.incl[c] = t.total;
+    if (64 * c < B) {  // (uniform)
+      t.incl[c] += wave_incl_scan(t.cnt[c], lane);
+      t.total = __builtin_amdgcn_readlane(t.incl[c], 63);  // scalar
+    }
+  }
+  return t;
+}
+
+// Value of lane (b % 64) of chunk b / 64 (b wave-uniform): a lane read, no
+// memory access.
+__device__ __forceinline__ int seq_value(const int (&v)[kBalancedMaxB / 64], int b) {
+  const int c = b >> 6;
+  const int x = c == 0 ? v[0] : c == 1 ? v[1] : c == 2 ? v[2] : v[3];
+  return __builtin_amdgcn_readlane(x, b & 63);
+}
+
+// Tiles per workgroup (the host keeps TT + P and P * C_min below 2^31).
+__device__ __forceinline__ int chunk_tiles(int TT, int P, int C_min) {
+  const int c = (TT + P - 1) / P;
+  return c > C_min ? c : C_min;
+}
+
 template <bool BF16>
 __device__ __forceinline__ void store_out(void *outp, size_t idx, float x) {
   if constexpr (BF16) {
@@ -196,17 +250,17 @@ __device__ __forceinline__ void store_out(void *outp, size_t idx, float x) {
 
 // Shared ending. fin_m/fin_l/fin_o (LDS) hold this workgroup's merged
 // running max, sum and unnormalised output of the G query heads of (b, g).
-// A sequence with a single split is finished here; otherwise the partial is
-// written for the combine kernel.
+// A piece that is the whole (b, g) (direct) is finished here; otherwise the
+// partial is written to slot s of (b, g) for the combine kernel.
 template <bool BF16, int D, int G, int NT>
 __device__ __forceinline__ void finish(const float *fin_m, const float *fin_l,
-                                       const float *fin_o, const Item &it,
+                                       const float *fin_o, bool direct,
                                        int b, int g, int s, int Hq,
                                        int splits, void *outp, float *ws_ml,
                                        float *ws_o) {
   const int tid = threadIdx.x;
   const size_t head0 = (size_t)b * Hq + (size_t)g * G;
-  if (it.n_split == 1) {
+  if (direct) {
     for (int i = tid; i < G * D; i += NT) {
       const int h = i / D, d = i % D;
       store_out<BF16>(outp, (head0 + h) * D + d, fin_o[h * D + d] / fin_l[h]);
@@ -248,11 +302,18 @@ struct Bf16Tile {
   static_assert(NOCT * (D / 8) == 64, "one V transpose item per lane");
 };
 
+// A piece of work: rows [row0, row1) of kv head g of sequence b (valid length
+// L); direct: the piece is the whole (b, g), whose output it writes, else its
+// partial goes to slot `slot` of (b, g). valid = 0: no piece.
+struct Piece {
+  int b, g, row0, row1, L, slot, direct, valid;
+};
+
 // MODE: 0 = contiguous cache, 1 = contiguous cache with the fused append,
 // 2 = paged cache, 3 = fused append with the rotary embedding of the query
 // and the new key.
 template <int D, int G, int MODE>
-__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     const uint16_t *__restrict__ qg, const uint16_t *__restrict__ kg,
     const uint16_t *__restrict__ vg, const int32_t *__restrict__ seq_lens,
     int position_id, void *__restrict__ outp, float *__restrict__ ws_ml,
@@ -261,7 +322,8 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     const uint16_t *__restrict__ knew, const uint16_t *__restrict__ vnew,
     uint16_t *kw, uint16_t *vw, const int32_t *__restrict__ block_table,
     int max_blocks, int page_size, int num_pages, int head_major,
-    const float *__restrict__ rcos, const float *__restrict__ rsin) {
+    const float *__restrict__ rcos, const float *__restrict__ rsin, int B,
+    int balanced, int P, int C_min) {
   constexpr bool APPEND = MODE == 1 || MODE == 3;
   constexpr bool PAGED = MODE == 2;
   constexpr bool ROPE = MODE == 3;
@@ -275,14 +337,6 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   __shared__ float fin_m[G], fin_l[G];
   __shared__ __attribute__((aligned(16))) uint16_t krot[ROPE ? D : 8];  // rotated new key
 
-  const Unit un = locate_unit(seq_lens, gridDim.y, Hkv, max_length, split_rows);
-  if (un.b < 0) return;
-  const int g = un.g, b = un.b, s = un.s;
-  const Item it = make_item(seq_lens, b, position_id, max_length, split_rows, s);
-  if (it.row0 >= it.L) {
-    if (it.L == 0 && s == 0) write_zero_rows<true, D, G, kThreads>(outp, b, g, Hq);
-    return;
-  }
   const int tid = threadIdx.x;
   // (uniform wave index in a scalar register where the paged tile lookup
   // depends on it)
@@ -290,23 +344,111 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   const int l = tid % 64;
   const int li = l % 16;   // query column / row within a 16-row block
   const int lg = l / 16;   // lane group (k slots 8*lg..8*lg+7)
+  const int oct = l % T::NOCT;  // V transpose item: rows 8*oct..8*oct+7
+  const int ch = l / T::NOCT;   //                   dims 8*ch..8*ch+7
+  uint16_t *vt = reinterpret_cast<uint16_t *>(smem + w * T::VT_BYTES);
 
-  // Query heads of the group as the B operand of Sᵀ = K·Qᵀ (column li).
-  // Rotary embedding: chunk ks of a lane (elements ks*32 + 8*lg ...) pairs
-  // with chunk ks + KS/2 of the same lane (D/2 further on).
-  // (the rotation waits for the tables; it is made after the first tile's
-  // loads are issued so that their latency overlaps it)
+  // Paged caches: row r of sequence b is row r % page_size of page
+  // block_table[b][r / page_size] (clamped to the pages that exist), pages
+  // token-major [page][row][Hkv][D] (consecutive rows of one kv head Hkv*D
+  // elements apart) or head-major [page][Hkv][row][D] (rows of a head
+  // contiguous). A tile (BN rows from a multiple of BN) never straddles a
+  // page. (The lookup is made on wave-uniform values so that it is a scalar
+  // load: a vector load would complete in order behind the K/V loads in
+  // flight.)
+  const size_t prs = head_major ? (size_t)D : (size_t)Hkv * D;
+  auto page_of = [&](int bu, int t0) {
+    const int tu = __builtin_amdgcn_readfirstlane(t0);
+    const int pg = block_table[(size_t)bu * max_blocks + tu / page_size];
+    return min(max(pg, 0), num_pages - 1);
+  };
+  auto page_tile = [&](const uint16_t *base, int gu, int pg, int t0) {
+    const int tu = __builtin_amdgcn_readfirstlane(t0);
+    return base + (head_major ? (((size_t)pg * Hkv + gu) * page_size + tu % page_size) * D
+                              : ((size_t)pg * page_size + tu % page_size) * prs + (size_t)gu * D);
+  };
+
+  // Where the rows of a piece come from. Appending: the sequence's last valid
+  // row (arow) is the new token; its K and V are read from knew / vnew, so no
+  // workgroup reads that cache row while it is being written.
+  struct Src {
+    const uint16_t *kb, *vb, *kn, *vn;
+    int b, g, last_row, arow;
+  };
+  auto src_of = [&](const Piece &p) {
+    Src s;
+    const size_t kvbase = ((size_t)p.b * Hkv + p.g) * (size_t)max_length * D;
+    s.kb = kg + kvbase;
+    s.vb = vg + kvbase;
+    s.kn = knew + ((size_t)p.b * Hkv + p.g) * D;
+    s.vn = vnew + ((size_t)p.b * Hkv + p.g) * D;
+    s.b = p.b;
+    s.g = p.g;
+    s.last_row = p.row1 - 1;  // rows are clamped to the piece (masked later)
+    s.arow = APPEND ? p.L - 1 : -1;
+    return s;
+  };
+
+  u32x4_t kf[NKB][KS], vr[8], qv[KS];
   bf16x8_t qf[KS];
-  u32x4_t qv[KS];
-  {
-    const uint16_t *qrow = qg + ((size_t)b * Hq + (size_t)g * G + li) * D;
+  auto load_q = [&](const Piece &p) {
+    const uint16_t *qrow = qg + ((size_t)p.b * Hq + (size_t)p.g * G + li) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qv[ks] = u32x4_t{0u, 0u, 0u, 0u};
       if (li < G) qv[ks] = *reinterpret_cast<const u32x4_t *>(qrow + ks * 32 + 8 * lg);
-      qf[ks] = as_bf16x8(qv[ks]);
     }
-  }
+  };
+  auto load_k = [&](const Src &s, int t0, int pg) {
+    const uint16_t *kt = PAGED ? page_tile(kg, s.g, pg, t0) : nullptr;
+#pragma unroll
+    for (int kb16 = 0; kb16 < NKB; ++kb16) {
+      const int row = min(t0 + kb16 * 16 + li, s.last_row);
+      const uint16_t *src = PAGED ? kt + (size_t)(row - t0) * prs
+                                  : (APPEND && row == s.arow ? s.kn : s.kb + (size_t)row * D);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[kb16][ks] = ldnt(src + ks * 32 + 8 * lg);
+    }
+  };
+  auto load_v = [&](const Src &s, int t0, int pg) {
+    const uint16_t *vtl = PAGED ? page_tile(vg, s.g, pg, t0) : nullptr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = min(t0 + 8 * oct + i, s.last_row);
+      const uint16_t *src = PAGED ? vtl + (size_t)(row - t0) * prs
+                                  : (APPEND && row == s.arow ? s.vn : s.vb + (size_t)row * D);
+      vr[i] = ldnt(src + 8 * ch);
+    }
+  };
+  // Runs piece `cur`. Each wave walks its tiles t0 = row0 + w*BN + 4*BN*i;
+  // the next tile's K is loaded as soon as the score products have read the
+  // current K registers and its V as soon as the current V rows are in LDS,
+  // so both loads run during the softmax and P·V of this tile. (Loading the
+  // first tile of the workgroup's next piece there as well, so that the
+  // loads stay in flight through the merge of the four waves, was measured
+  // 1-2 % slower on the ragged batch and batches of equal lengths.)
+  auto run = [&](const Piece &cur_) __attribute__((always_inline)) {
+  // (the piece is the same in every lane; held in scalar registers, the
+  // addresses and loop bounds derived from it stay scalar too)
+  Piece cur;
+  cur.b = __builtin_amdgcn_readfirstlane(cur_.b);
+  cur.g = __builtin_amdgcn_readfirstlane(cur_.g);
+  cur.row0 = __builtin_amdgcn_readfirstlane(cur_.row0);
+  cur.row1 = __builtin_amdgcn_readfirstlane(cur_.row1);
+  cur.L = __builtin_amdgcn_readfirstlane(cur_.L);
+  cur.slot = __builtin_amdgcn_readfirstlane(cur_.slot);
+  cur.direct = __builtin_amdgcn_readfirstlane(cur_.direct);
+  const int b = cur.b, g = cur.g, row0 = cur.row0, row1 = cur.row1;
+  const Src cs = src_of(cur);
+
+  // Query heads of the group as the B operand of Sᵀ = K·Qᵀ (column li).
+  // Rotary embedding: chunk ks of a lane (elements ks*32 + 8*lg ...) pairs
+  // with chunk ks + KS/2 of the same lane (D/2 further on). (The rotation
+  // waits for the tables; it is made after the first tile's loads are issued
+  // so that their latency overlaps it.)
+  load_q(cur);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(qv[ks]);
   auto rotate_q = [&]() {
     if (li < G) {
       const float *cb = rcos + (size_t)b * D, *sb = rsin + (size_t)b * D;
@@ -322,61 +464,31 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(qv[ks]);
   };
 
-  const size_t kvbase = ((size_t)b * Hkv + g) * (size_t)max_length * D;
-  const uint16_t *kb = kg + kvbase;
-  const uint16_t *vb = vg + kvbase;
-  // Paged caches: row r of sequence b is row r % page_size of page
-  // block_table[b][r / page_size] (clamped to the pages that exist), pages
-  // token-major [page][row][Hkv][D] (consecutive rows of one kv head Hkv*D
-  // elements apart) or head-major [page][Hkv][row][D] (rows of a head
-  // contiguous). A tile (BN rows from a multiple of BN) never straddles a
-  // page.
-  const size_t prs = head_major ? (size_t)D : (size_t)Hkv * D;
-  // (the lookup is made on wave-uniform values so that it is a scalar load:
-  // a vector load would complete in order behind the K/V loads in flight)
-  const int bu = __builtin_amdgcn_readfirstlane(b);
-  const int gu = __builtin_amdgcn_readfirstlane(g);
-  auto page_of = [&](int t0) {
-    const int tu = __builtin_amdgcn_readfirstlane(t0);
-    const int pg = block_table[(size_t)bu * max_blocks + tu / page_size];
-    return min(max(pg, 0), num_pages - 1);
-  };
-  auto page_tile = [&](const uint16_t *base, int pg, int t0) {
-    const int tu = __builtin_amdgcn_readfirstlane(t0);
-    return base + (head_major ? (((size_t)pg * Hkv + gu) * page_size + tu % page_size) * D
-                              : ((size_t)pg * page_size + tu % page_size) * prs + (size_t)gu * D);
-  };
-  // Appending: the sequence's last valid row is the new token. Its K and V
-  // are read from knew / vnew (so no workgroup reads that cache row while it
-  // is being written) and split 0 stores them into the cache. With the rotary
-  // embedding split 0 and the workgroup whose split holds the new row rotate
-  // the new key (into LDS, krot, for the latter); the wave whose tile holds
-  // the new row takes that row's K from there.
-  const int arow = APPEND ? it.L - 1 : -1;
-  const uint16_t *kn = knew + ((size_t)b * Hkv + g) * D;
-  const uint16_t *vn = vnew + ((size_t)b * Hkv + g) * D;
-  const bool holds_arow = ROPE && it.row0 <= arow && arow < it.row1;  // uniform
-  if (APPEND && (s == 0 || holds_arow)) {
+  // The piece that starts at row 0 stores the new token's K and V into the
+  // cache. With the rotary embedding that piece and the piece that holds the
+  // new row rotate the new key (into LDS, krot, for the latter); the wave
+  // whose tile holds the new row takes that row's K from there.
+  const int arow = cs.arow;
+  const bool holds_arow = ROPE && row0 <= arow && arow < row1;  // uniform
+  if (APPEND && (row0 == 0 || holds_arow)) {
+    const size_t kvbase = ((size_t)b * Hkv + g) * (size_t)max_length * D;
     for (int i = tid; i < D / 8; i += kThreads) {
-      u32x4_t kx = *reinterpret_cast<const u32x4_t *>(kn + 8 * i);
+      u32x4_t kx = *reinterpret_cast<const u32x4_t *>(cs.kn + 8 * i);
       if constexpr (ROPE) {
         const int j0 = 8 * i;
         const bool lo = j0 < D / 2;
-        const u32x4_t px = *reinterpret_cast<const u32x4_t *>(kn + (lo ? j0 + D / 2 : j0 - D / 2));
+        const u32x4_t px = *reinterpret_cast<const u32x4_t *>(cs.kn + (lo ? j0 + D / 2 : j0 - D / 2));
         kx = rope_bf16x8(kx, px, rcos + (size_t)b * D + j0, rsin + (size_t)b * D + j0, lo);
         if (holds_arow) *reinterpret_cast<u32x4_t *>(&krot[j0]) = kx;
       }
-      if (s == 0) {
+      if (row0 == 0) {
         *reinterpret_cast<u32x4_t *>(kw + kvbase + (size_t)arow * D + 8 * i) = kx;
         *reinterpret_cast<u32x4_t *>(vw + kvbase + (size_t)arow * D + 8 * i) =
-            *reinterpret_cast<const u32x4_t *>(vn + 8 * i);
+            *reinterpret_cast<const u32x4_t *>(cs.vn + 8 * i);
       }
     }
     if (holds_arow) __syncthreads();  // krot complete (uniform over the workgroup)
   }
-  uint16_t *vt = reinterpret_cast<uint16_t *>(smem + w * T::VT_BYTES);
-  const int oct = l % T::NOCT;  // V transpose item: rows 8*oct..8*oct+7
-  const int ch = l / T::NOCT;   //                   dims 8*ch..8*ch+7
 
   f32x4_t o[NDB];
 #pragma unroll
@@ -384,36 +496,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
   float m = kNegInf;
   float lsum = 0.f;
 
-  // Tiles of this wave: t0 = row0 + w*BN + 4*BN*i. The next tile's K is
-  // loaded as soon as the score products have read the current K registers,
-  // and its V as soon as the current V rows are in LDS, so both loads run
-  // during the softmax and P·V of this tile. Rows are clamped to the split
-  // (a partial last tile reads valid rows; they are masked).
-  const int last_row = it.row1 - 1;
-  u32x4_t kf[NKB][KS], vr[8];
-  auto load_k = [&](int t0, int pg) {
-    const uint16_t *kt = PAGED ? page_tile(kg, pg, t0) : nullptr;
-#pragma unroll
-    for (int kb16 = 0; kb16 < NKB; ++kb16) {
-      const int row = min(t0 + kb16 * 16 + li, last_row);
-      const uint16_t *src = PAGED ? kt + (size_t)(row - t0) * prs
-                                  : (APPEND && row == arow ? kn : kb + (size_t)row * D);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[kb16][ks] = ldnt(src + ks * 32 + 8 * lg);
-    }
-  };
-  auto load_v = [&](int t0, int pg) {
-    const uint16_t *vtl = PAGED ? page_tile(vg, pg, t0) : nullptr;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = min(t0 + 8 * oct + i, last_row);
-      const uint16_t *src = PAGED ? vtl + (size_t)(row - t0) * prs
-                                  : (APPEND && row == arow ? vn : vb + (size_t)row * D);
-      vr[i] = ldnt(src + 8 * ch);
-    }
-  };
+  // tnext >= 0: load that tile once this tile's registers are free
   auto compute_tile = [&](int t0, int tnext, int pgnext) {
-    const bool full = t0 + BN <= it.row1;
+    const bool full = t0 + BN <= row1;
     if constexpr (ROPE) {
       if (t0 <= arow && arow < t0 + BN) {  // this tile holds the new token
 #pragma unroll
@@ -435,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
         sc[kb16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             as_bf16x8(kf[kb16][ks]), qf[ks], sc[kb16], 0, 0, 0);
     }
-    if (tnext >= 0) load_k(tnext, pgnext);
+    if (tnext >= 0) load_k(cs, tnext, pgnext);
     // ---- V rows -> Vᵀ in LDS (keys 8*oct..8*oct+7 of dims 8*ch..8*ch+7) ----
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -452,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
       dst[0] = u32x2_t{pk[0], pk[1]};
       dst[1] = u32x2_t{pk[2], pk[3]};
     }
-    if (tnext >= 0) load_v(tnext, pgnext);
+    if (tnext >= 0) load_v(cs, tnext, pgnext);
     // ---- online softmax -----------------------------------------------------------
     float mx = kNegInf;
 #pragma unroll
@@ -460,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float x = sc[kb16][r] * qk_scale;
-        if (!full && t0 + kb16 * 16 + 4 * lg + r >= it.row1) x = kNegInf;
+        if (!full && t0 + kb16 * 16 + 4 * lg + r >= row1) x = kNegInf;
         sc[kb16][r] = x;
         mx = fmaxf(mx, x);
       }
@@ -506,18 +591,18 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  for (int t0 = it.row0 + w * BN, first = 1; t0 < it.row1; t0 += 4 * BN, first = 0) {
+  for (int t0 = row0 + w * BN, first = 1; t0 < row1; t0 += 4 * BN, first = 0) {
     if (first) {
-      const int pg0 = PAGED ? page_of(t0) : 0;
-      load_k(t0, pg0);
-      load_v(t0, pg0);
+      const int pg0 = PAGED ? page_of(b, t0) : 0;
+      load_k(cs, t0, pg0);
+      load_v(cs, t0, pg0);
       if constexpr (ROPE) rotate_q();
     }
     const int t1 = t0 + 4 * BN;
     // (the next tile's page is looked up before this tile's products, so the
     // scalar load has completed when the next tile's loads are issued)
-    const int pg1 = PAGED && t1 < it.row1 ? page_of(t1) : 0;
-    compute_tile(t0, t1 < it.row1 ? t1 : -1, pg1);
+    const int pg1 = PAGED && t1 < row1 ? page_of(b, t1) : 0;
+    compute_tile(t0, t1 < row1 ? t1 : -1, pg1);
   }
 
   // ---- merge the 4 waves -----------------------------------------------------------
@@ -567,8 +652,83 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(
     if (i < G * D) fo[i] = acc[j];
   }
   __syncthreads();
-  finish<true, D, G, kThreads>(fin_m, fin_l, fo, it, b, g, s, Hq, splits,
-                               outp, ws_ml, ws_o);
+  finish<true, D, G, kThreads>(fin_m, fin_l, fo, cur.direct != 0, b, g, cur.slot, Hq,
+                               splits, outp, ws_ml, ws_o);
+  };  // run
+
+  if (balanced) {
+    // Tiles [wg*C, min((wg+1)*C, TT)) of the batch's (b, g, tile) order.
+    const BatchTiles bt = batch_tiles(seq_lens, B, max_length, BN);
+    const int TT = Hkv * bt.total;
+    const int C = chunk_tiles(TT, P, C_min);
+    // workgroup i runs on XCD i % 8: chunk (i % 8) * (P / 8) + i / 8 gives
+    // each XCD a contiguous run of chunks (P is a multiple of 8)
+    const int wg = (int)(blockIdx.x % 8) * (P / 8) + (int)blockIdx.x / 8;
+    const int lo = wg * C;
+    if (lo >= TT) return;
+    const int hi = min(lo + C, TT);
+    // the sequence of tile lo: the first b with Hkv * (tiles up to b) > lo
+    int b = 0;
+#pragma unroll
+    for (int c = 0; c < kBalancedMaxB / 64; ++c) {
+      const unsigned long long hit = __ballot(Hkv * bt.incl[c] > lo);
+      if (hit != 0ull) {
+        b = 64 * c + __ffsll(hit) - 1;
+        break;
+      }
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    int nb = seq_value(bt.cnt, b);
+    int Pb = seq_value(bt.incl, b) - nb;
+    int Lb = seq_value(bt.len, b);
+    int g = (lo - Hkv * Pb) / nb;
+    // the piece of (b, g) from tile `from` up to the range's end; its end tile
+    auto piece_at = [&](int from, int &end) {
+      const int start = Hkv * Pb + g * nb;  // first tile of (b, g)
+      const int t_end = min(nb, hi - start);
+      const int first = start / C;          // workgroup holding tile 0 of (b, g)
+      Piece p;
+      p.b = b;
+      p.g = g;
+      p.row0 = (from - start) * BN;
+      p.row1 = min(t_end * BN, Lb);
+      p.L = Lb;
+      p.slot = wg - first;
+      p.direct = first == (start + nb - 1) / C;
+      p.valid = 1;
+      end = start + t_end;
+      return p;
+    };
+    int from = lo, end;
+    for (;;) {
+      run(piece_at(from, end));
+      if (end >= hi) break;
+      // the next piece is tile 0 of the next (b, g)
+      if (++g == Hkv) {  // next sequence that holds rows
+        g = 0;
+        Pb += nb;
+        nb = 0;
+        while (nb == 0 && b + 1 < B) {
+          ++b;
+          Lb = seq_value(bt.len, b);
+          nb = (Lb + BN - 1) / BN;
+        }
+        if (nb == 0) break;  // (not reached: tiles remain, so rows do)
+      }
+      from = end;
+      __syncthreads();  // the next piece reuses the LDS
+    }
+    return;
+  }
+
+  const Unit un = locate_unit(seq_lens, gridDim.y, Hkv, max_length, split_rows);
+  if (un.b < 0) return;
+  const Item it = make_item(seq_lens, un.b, position_id, max_length, split_rows, un.s);
+  if (it.row0 >= it.L) {
+    if (it.L == 0 && un.s == 0) write_zero_rows<true, D, G, kThreads>(outp, un.b, un.g, Hq);
+    return;
+  }
+  run(Piece{un.b, un.g, it.row0, it.row1, it.L, un.s, it.n_split == 1, 1});
 }
 
 // ---------------------------------------------------------------------------
@@ -737,8 +897,8 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(
     }
     __syncthreads();
   }
-  finish<false, D, G, kThreads>(fin_m, fin_l, sm_o, it, b, g, s, Hq, splits,
-                                outp, ws_ml, ws_o);
+  finish<false, D, G, kThreads>(fin_m, fin_l, sm_o, it.n_split == 1, b, g, s,
+                                Hq, splits, outp, ws_ml, ws_o);
 }
 
 // ---------------------------------------------------------------------------
@@ -760,16 +920,33 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     const float *__restrict__ ws_ml, const float *__restrict__ ws_o,
     const int32_t *__restrict__ seq_lens, int position_id,
     void *__restrict__ outp, int Hq, int max_length, int split_rows,
-    int splits) {
+    int splits, int Hkv, int balanced, int P, int C_min) {
   constexpr int PER = D / 64;  // output dimensions per lane
   static_assert(PER == 1 || PER == 2, "D is 64 or 128");
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const Item it = make_item(seq_lens, b, position_id, max_length, split_rows, 0);
-  const int n = it.n_split;
-  if (n <= 1) return;  // finished by the split kernel (or zero rows)
   const int lane = threadIdx.x;
   const size_t head = (size_t)b * Hq + hq;
+  int n;  // partials of (b, hq)
+  if (balanced) {
+    // the pieces of (b, g) under the balanced schedule (above); a sequence
+    // without rows gets its zero output row here
+    constexpr int BN = 4096 / D;
+    const BatchTiles bt = batch_tiles(seq_lens, gridDim.y, max_length, BN);
+    const int nb = seq_value(bt.cnt, b);
+    const int Pb = seq_value(bt.incl, b) - nb;
+    if (nb == 0) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) store_out<BF16>(outp, head * D + lane * PER + e, 0.f);
+      return;
+    }
+    const int C = chunk_tiles(Hkv * bt.total, P, C_min);
+    const int start = Hkv * Pb + (hq / (Hq / Hkv)) * nb;
+    n = (start + nb - 1) / C - start / C + 1;
+  } else {
+    n = make_item(seq_lens, b, position_id, max_length, split_rows, 0).n_split;
+  }
+  if (n <= 1) return;  // finished by the split kernel (or zero rows)
   const float2 *ml = reinterpret_cast<const float2 *>(ws_ml + head * splits * 2);
   const float *o = ws_o + head * splits * D + lane * PER;
   const int last = n - 1;
@@ -845,7 +1022,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
 
 template <bool BF16, int D, int G, int MODE>
 void launch_split(const DecodeArgs &a, hipStream_t stream) {
-  dim3 grid(a.Hkv, a.B, a.plan.splits);
+  const dim3 grid = a.plan.balanced ? dim3(a.plan.P) : dim3(a.Hkv, a.B, a.plan.splits);
   if constexpr (BF16) {
     decode_bf16_kernel<D, G, MODE><<<grid, kThreads, 0, stream>>>(
         static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
@@ -855,7 +1032,7 @@ void launch_split(const DecodeArgs &a, hipStream_t stream) {
         static_cast<const uint16_t *>(a.k_new), static_cast<const uint16_t *>(a.v_new),
         static_cast<uint16_t *>(a.k_w), static_cast<uint16_t *>(a.v_w),
         a.block_table, a.max_blocks, a.page_size, a.num_pages, a.head_major,
-        a.rope_cos, a.rope_sin);
+        a.rope_cos, a.rope_sin, a.B, a.plan.balanced, a.plan.P, a.plan.C_min);
   } else {
     static_assert(MODE != 2, "paged caches are bf16 only");
     decode_f32_kernel<D, G, MODE == 1 || MODE == 3, MODE == 3><<<grid, kThreads, 0, stream>>>(
@@ -884,10 +1061,11 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
     launch_split<BF16, D, G, 0>(a, stream);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.plan.splits <= 1) return e;
+  if (e != hipSuccess || (!a.plan.balanced && a.plan.splits <= 1)) return e;
   decode_combine_kernel<BF16, D><<<dim3(a.Hq, a.B), 64, 0, stream>>>(
       a.ws_ml, a.ws_o, a.seq_lens, a.position_id, a.out, a.Hq, a.max_length,
-      a.plan.split_rows, a.plan.splits);
+      a.plan.split_rows, a.plan.splits, a.Hkv, a.plan.balanced, a.plan.P,
+      a.plan.C_min);
   return hipGetLastError();
 }
 

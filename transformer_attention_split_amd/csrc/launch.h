@@ -14,9 +14,18 @@ constexpr int kDecodeThreads = 256;
 // one weight per split in LDS).
 constexpr int kDecodeMaxSplits = 1024;
 
+// Largest batch the balanced schedule takes (its prefix sums over the
+// sequence lengths are one register per 64 sequences).
+constexpr int kBalancedMaxB = 256;
+
 struct DecodePlan {
   int split_rows;  // cache rows per split work item
-  int splits;      // split work items per (b, kv head) in the grid
+  int splits;      // split work items per (b, kv head) in the grid; balanced:
+                   // partial slots per (b, query head)
+  // Balanced schedule (bf16 with per-sequence lengths, B <= kBalancedMaxB):
+  // P workgroups, each at least C_min wave tiles of 4096/D rows.
+  int balanced = 0;
+  int P = 0, C_min = 0;
 };
 
 struct DecodeArgs {

@@ -56,20 +56,6 @@ __device__ __forceinline__ uint32_t order32(float f) {
 }
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// Inclusive prefix sum over the 64 lanes: DPP row shifts inside each
-// 16-lane row (out-of-row sources contribute 0), then the totals of the
-// earlier rows read with readlane.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x, int lane) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);
-  const uint32_t t0 = __builtin_amdgcn_readlane(x, 15);
-  const uint32_t t1 = __builtin_amdgcn_readlane(x, 31);
-  const uint32_t t2 = __builtin_amdgcn_readlane(x, 47);
-  return x + (lane >= 16 ? t0 : 0u) + (lane >= 32 ? t1 : 0u) + (lane >= 48 ? t2 : 0u);
-}
-
 // LDS writes of the wave become visible to all its lanes.
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
