@@ -772,7 +772,7 @@ def main():
     traffic = committed_traffic("decode_ragged_b64_traffic.txt",
                                 "decode.hip")
     roofline = {
-        "kernel": "decode_bf16_kernel<128, 4, 0> + decode_combine_kernel<true, 128> (one attn_decode call)",
+        "kernel": "decode_bf16_kernel<128, 4, 0, true> + decode_combine_kernel<true, 128> (one attn_decode call)",
         "bound": "hbm", "achieved": round(dec_gbps, 1),
         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),

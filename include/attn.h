@@ -342,12 +342,12 @@ attn_status attn_topk_causal(const float *q, const float *k, const float *v, flo
  * array of the library instead of a caller workspace. Arguments, result and
  * supported set are attn_decode's, without workspace / workspace_bytes.
  *
- * - The library holds one scratch array of 16 MiB on every GPU it runs on,
+ * - The library holds one scratch array of 64 MiB on every GPU it runs on,
  *   from the first call on that GPU until the process ends; this call itself
  *   allocates nothing.
- * - Sizes whose split partials need more than 16 MiB
+ * - Sizes whose split partials need more than 64 MiB
  *   (attn_decode_workspace_bytes(B, Hq, Hkv, D, max_length, split_rows) >
- *   16 MiB) return ATTN_E_WORKSPACE before any launch.
+ *   64 MiB) return ATTN_E_WORKSPACE before any launch.
  * - Every call on one GPU uses that GPU's same array: calls that may overlap
  *   on one GPU (different streams, or host threads racing on one stream)
  *   race on the partials and give wrong results. Serialise them. No initial

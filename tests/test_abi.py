@@ -130,9 +130,9 @@ def decode_noalloc(**kw):
     (dict(out=None), E_ARG),
     (dict(q=P + 8), E_ARG),
     # the split partials of 64 ragged sequences at 1-row splits need far more
-    # than the 16 MiB static scratch
+    # than the 64 MiB static scratch
     (dict(B=64, seq_lens=P, split_rows=1), E_WS),
-    (dict(B=1024, Hq=64, Hkv=8, seq_lens=P), E_WS),
+    (dict(B=4096, Hq=64, Hkv=8, seq_lens=P), E_WS),
 ])
 def test_decode_noalloc_rejects_before_any_hip_call(kw, status):
     assert decode_noalloc(**kw) == status
@@ -143,11 +143,11 @@ def test_decode_noalloc_rejects_before_any_hip_call(kw, status):
 
 
 def test_decode_noalloc_scratch_limit_is_the_workspace_size():
-    # 16 MiB is the limit: the ragged B=64, Hq=32, Hkv=8, D=128 batch at
+    # 64 MiB is the limit: the ragged B=64, Hq=32, Hkv=8, D=128 batch at
     # max_length 8192 fits with the automatic split
     need = lib.attn_decode_workspace_bytes(64, 32, 8, 128, 8192, 0)
-    assert 0 < need <= 16 << 20
-    assert lib.attn_decode_workspace_bytes(64, 32, 8, 128, 8192, 1) > 16 << 20
+    assert 0 < need <= 64 << 20
+    assert lib.attn_decode_workspace_bytes(64, 32, 8, 128, 8192, 1) > 64 << 20
 
 
 def test_decode_noalloc_batch_zero_is_a_noop():

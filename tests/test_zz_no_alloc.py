@@ -56,10 +56,10 @@ def test_noalloc_two_calls_second_smaller():
 
 def test_noalloc_rejects_sizes_beyond_the_scratch():
     q = torch.zeros(64, 32, 128, dtype=torch.bfloat16, device="cuda")
-    k = torch.zeros(64, 8, 64, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(64, 8, 256, 128, dtype=torch.bfloat16, device="cuda")
     lens = torch.ones(64, dtype=torch.int32, device="cuda")
     with pytest.raises(tas.AttnArgError) as ei:
-        # 1-row splits of 64 sequences: partials far beyond 16 MiB
+        # 1-row splits of 64 sequences of 256 rows: partials far beyond 64 MiB
         tas.attn_decode_noalloc(q, k, k, torch.empty_like(q), seq_lens=lens,
                                 split_rows=1)
     assert ei.value.status == tas.ATTN_E_WORKSPACE

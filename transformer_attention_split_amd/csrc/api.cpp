@@ -105,25 +105,24 @@ attn::DecodePlan plan_decode(int B, int Hkv, int D, int max_length,
 }
 
 // Balanced schedule (ragged bf16 batches of at most kBalancedMaxB sequences;
-// the device side is described in decode.hip): P = two workgroups per CU,
-// the split kernel's occupancy, so that every workgroup of the launch is
-// resident and streams from start to end (fewer when the batch at full
-// length holds fewer ranges of C_min tiles); each takes at least C_min wave
-// tiles. Workgroup i takes range (i % 8) * (P / 8) + i / 8, so that each
-// XCD streams a contiguous run of ranges (160.9 against 161.9 us on the
-// ragged batch below, 167.5 against 172.4 us with its sequences sorted by
-// length). Forcing split_rows sets C_min = ceil(split_rows / tile); otherwise
-// C_min is two rounds of the four wave tiles (one round while the whole
-// batch at full length fits one round per CU) or an eighth of a
-// workgroup's share of the batch at full length, whichever is larger, so
-// that batches of shorter sequences still occupy the grid. C_min is at least
-// ceil(n_max / (kDecodeMaxSplits - 1)), which bounds the pieces of one
-// (b, kv head) by S = ceil(n_max / C_min) + 1 <= kDecodeMaxSplits (n_max:
-// wave tiles of max_length rows). Measured per call (split and combine) on
-// 64 uniformly ragged sequences of up to 8192 rows (Hkv 8, D 128): 160.9 us
-// against 171.1 us with one 896-row split per workgroup, whose launch ended
-// in a tail of the longest sequences' last splits; 64 sequences of 4096
-// rows: 162.3 against 176.8 us.
+// the device side is described in decode.hip). Every wave is a worker that
+// streams an equal run of the batch's wave tiles (at least C_min of them),
+// across sequence ends, and writes one partial per piece it cuts: no merge
+// of waves, no workgroup barrier. Two workgroups per CU, the split kernel's
+// occupancy, so that every worker is resident from start to end: P = 4 *
+// 512 workers (fewer when the batch at full length holds fewer runs of
+// C_min tiles; P / 4 a multiple of 8, the XCD count, each of which takes a
+// contiguous run of workers). Forcing split_rows sets C_min =
+// ceil(split_rows / tile); otherwise C_min is 4 tiles or an eighth of a
+// worker's share of the batch at full length, whichever is larger, so that
+// batches of shorter sequences still occupy the grid while a partial
+// (G*(D+2) floats) stays small against the rows it covers. C_min is at
+// least ceil(n_max / (kDecodeMaxSplits - 1)), which bounds the pieces of
+// one (b, kv head) by S = ceil(n_max / C_min) + 1 <= kDecodeMaxSplits
+// (n_max: wave tiles of max_length rows). Per call on 64 uniformly ragged
+// sequences of up to 8192 rows (Hkv 8, D 128): 159.1-159.7 us, against
+// 168-172 us with one split per workgroup and 161-164 us with equal runs per
+// workgroup whose four waves merge at every piece end.
 struct BalancedPlan {
   bool ok;
   int P, C_min, S;
@@ -135,16 +134,16 @@ BalancedPlan plan_balanced(int B, int Hkv, int D, int max_length,
   const long tile = 4096 / D;
   const long n_max = ceil_div(max_length, tile);
   const long tt_max = (long)B * Hkv * n_max;
-  p.P = 2 * (int)kCUs;
+  p.P = 4 * 2 * (int)kCUs;
   // (one sequence has nothing to balance: its equal splits of the plain
-  // grid finish together, while a range that straddles two kv heads runs
+  // grid finish together, while a run that straddles two kv heads takes
   // two pieces in turn: 13.3 against 15.7 us at 8001 rows, Hkv 8, D 128)
   if (B < 2 || B > attn::kBalancedMaxB || tt_max + p.P > INT_MAX) return p;
   long cmin;
   if (split_rows > 0) {
     cmin = ceil_div(split_rows, tile);
   } else {
-    cmin = tt_max / 4 > kCUs ? 8 : 4;
+    cmin = 4;
     const long share = ceil_div(tt_max, 8L * p.P);
     if (share > cmin) cmin = share;
   }
@@ -152,9 +151,8 @@ BalancedPlan plan_balanced(int B, int Hkv, int D, int max_length,
   if (cmin < floor_tiles) cmin = floor_tiles;
   if (cmin > INT_MAX / p.P) cmin = INT_MAX / p.P;
   p.C_min = (int)cmin;
-  // no more workgroups than ranges of C_min tiles in the batch at full
-  // length (a multiple of 8, the XCD count)
-  const long need = (ceil_div(tt_max, cmin) + 7) / 8 * 8;
+  // no more workers than runs of C_min tiles in the batch at full length
+  const long need = (ceil_div(tt_max, cmin) + 31) / 32 * 32;
   if (need < p.P) p.P = (int)need;
   p.S = ceil_div(n_max, cmin) + 1;
   p.ok = true;
@@ -359,7 +357,7 @@ attn_status attn_decode(attn_dtype dtype, const void *q, const void *k_cache,
 // to the kernels.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr size_t kScratchBytes = size_t(64) << 20;
 constexpr int kMaxDevices = 64;
 void *g_scratch_dev[kMaxDevices];  // device address of scratch, per GPU
 hipError_t g_scratch_err[kMaxDevices];

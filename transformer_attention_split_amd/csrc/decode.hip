@@ -7,7 +7,10 @@
 // table). Query head h reads kv head h / G (G = Hq/Hkv), so each K and V row
 // is read once and serves the whole group of G query heads.
 //
-// Work item = (kv head g, sequence b, split s) = cache rows
+// Ragged bf16 batches of 2 to kBalancedMaxB sequences run the balanced
+// schedule described below its helpers: every wave streams an equal run of
+// the batch's tiles. Otherwise:
+// work item = (kv head g, sequence b, split s) = cache rows
 // [s*split_rows, min((s+1)*split_rows, L_b)). The grid is (Hkv, B, splits),
 // dispatched x fastest. With one length for the whole batch the split index
 // varies slowest: the round-robin dispatch over the 8 XCDs spreads every
@@ -185,15 +188,16 @@ __device__ __forceinline__ Unit locate_unit(const int32_t *seq_lens, int B,
 // ---------------------------------------------------------------------------
 // The work of the batch is the list of wave tiles (BN rows) of every
 // (sequence b, kv head g) in the order (b, g, tile): n_b = ceil(L_b / BN)
-// tiles per kv head of sequence b, TT = Hkv * sum_b n_b in all. Workgroup w
-// of the P launched takes the tiles [w*C, (w+1)*C), C = max(C_min,
-// ceil(TT / P)), so every workgroup streams the same number of rows (to
-// within one tile per piece) whatever the lengths, and a long sequence no
-// longer ends the launch alone. A range cuts one or more (b, g) into pieces.
-// A (b, g) inside one range is finished there; the others leave one partial
-// per piece, in slot w - first(b, g), first(b, g) = floor(start(b, g) / C),
-// start(b, g) = Hkv * P_b + g * n_b (P_b: the tiles of the sequences before
-// b), which the combine kernel finds from the same lengths.
+// tiles per kv head of sequence b, TT = Hkv * sum_b n_b in all. Every wave
+// is a worker: worker u of the P launched (four per workgroup) takes the
+// tiles [u*C, (u+1)*C), C = max(C_min, ceil(TT / P)), so every wave streams
+// the same number of rows whatever the lengths, and a long sequence no
+// longer ends the launch alone; no wave waits for another. A range cuts one
+// or more (b, g) into pieces. A (b, g) inside one range is finished there;
+// the others leave one partial per piece, in slot u - first(b, g),
+// first(b, g) = floor(start(b, g) / C), start(b, g) = Hkv * P_b + g * n_b
+// (P_b: the tiles of the sequences before b), which the combine kernel finds
+// from the same lengths.
 __device__ __forceinline__ int clamp_len(int L, int max_length) {
   return L < 0 ? 0 : (L > max_length ? max_length : L);
 }
@@ -311,8 +315,10 @@ struct Piece {
 
 // MODE: 0 = contiguous cache, 1 = contiguous cache with the fused append,
 // 2 = paged cache, 3 = fused append with the rotary embedding of the query
-// and the new key.
-template <int D, int G, int MODE>
+// and the new key. SOLO: the balanced schedule, every wave a worker of its
+// own (below); otherwise one work unit per workgroup, its four waves taking
+// every fourth tile and merging at the end.
+template <int D, int G, int MODE, bool SOLO>
 __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     const uint16_t *__restrict__ qg, const uint16_t *__restrict__ kg,
     const uint16_t *__restrict__ vg, const int32_t *__restrict__ seq_lens,
@@ -335,7 +341,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
   constexpr int LDS_BYTES = LDS_MAIN > LDS_FIN ? LDS_MAIN : LDS_FIN;
   __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
   __shared__ float fin_m[G], fin_l[G];
-  __shared__ __attribute__((aligned(16))) uint16_t krot[ROPE ? D : 8];  // rotated new key
+  // rotated new key (one per wave when the waves work alone)
+  __shared__ __attribute__((aligned(16))) uint16_t krot[ROPE ? (SOLO ? 4 : 1) * D : 8];
 
   const int tid = threadIdx.x;
   // (uniform wave index in a scalar register where the paged tile lookup
@@ -420,7 +427,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
       vr[i] = ldnt(src + 8 * ch);
     }
   };
-  // Runs piece `cur`. Each wave walks its tiles t0 = row0 + w*BN + 4*BN*i;
+  // Runs piece `cur`. Each wave walks its tiles t0 = row0 + w*BN + 4*BN*i
+  // (SOLO: all the piece's tiles, t0 = row0 + BN*i);
   // the next tile's K is loaded as soon as the score products have read the
   // current K registers and its V as soon as the current V rows are in LDS,
   // so both loads run during the softmax and P·V of this tile. (Loading the
@@ -440,6 +448,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
   cur.direct = __builtin_amdgcn_readfirstlane(cur_.direct);
   const int b = cur.b, g = cur.g, row0 = cur.row0, row1 = cur.row1;
   const Src cs = src_of(cur);
+  constexpr int WS = SOLO ? 1 : 4;  // waves sharing the piece's tiles
+  const int wofs = SOLO ? 0 : w;    // this wave's first tile of the piece
+  uint16_t *kr = krot + (ROPE && SOLO ? w * D : 0);
 
   // Query heads of the group as the B operand of Sᵀ = K·Qᵀ (column li).
   // Rotary embedding: chunk ks of a lane (elements ks*32 + 8*lg ...) pairs
@@ -472,14 +483,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
   const bool holds_arow = ROPE && row0 <= arow && arow < row1;  // uniform
   if (APPEND && (row0 == 0 || holds_arow)) {
     const size_t kvbase = ((size_t)b * Hkv + g) * (size_t)max_length * D;
-    for (int i = tid; i < D / 8; i += kThreads) {
+    for (int i = SOLO ? l : tid; i < D / 8; i += SOLO ? 64 : kThreads) {
       u32x4_t kx = *reinterpret_cast<const u32x4_t *>(cs.kn + 8 * i);
       if constexpr (ROPE) {
         const int j0 = 8 * i;
         const bool lo = j0 < D / 2;
         const u32x4_t px = *reinterpret_cast<const u32x4_t *>(cs.kn + (lo ? j0 + D / 2 : j0 - D / 2));
         kx = rope_bf16x8(kx, px, rcos + (size_t)b * D + j0, rsin + (size_t)b * D + j0, lo);
-        if (holds_arow) *reinterpret_cast<u32x4_t *>(&krot[j0]) = kx;
+        if (holds_arow) *reinterpret_cast<u32x4_t *>(&kr[j0]) = kx;
       }
       if (row0 == 0) {
         *reinterpret_cast<u32x4_t *>(kw + kvbase + (size_t)arow * D + 8 * i) = kx;
@@ -487,7 +498,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
             *reinterpret_cast<const u32x4_t *>(cs.vn + 8 * i);
       }
     }
-    if (holds_arow) __syncthreads();  // krot complete (uniform over the workgroup)
+    if (holds_arow) {  // krot complete (uniform over the workgroup / wave)
+      if constexpr (SOLO) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      } else {
+        __syncthreads();
+      }
+    }
   }
 
   f32x4_t o[NDB];
@@ -506,7 +525,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
           if (t0 + kb16 * 16 + li == arow) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-              kf[kb16][ks] = *reinterpret_cast<const u32x4_t *>(&krot[ks * 32 + 8 * lg]);
+              kf[kb16][ks] = *reinterpret_cast<const u32x4_t *>(&kr[ks * 32 + 8 * lg]);
           }
       }
     }
@@ -591,23 +610,46 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  for (int t0 = row0 + w * BN, first = 1; t0 < row1; t0 += 4 * BN, first = 0) {
+  for (int t0 = row0 + wofs * BN, first = 1; t0 < row1; t0 += WS * BN, first = 0) {
     if (first) {
       const int pg0 = PAGED ? page_of(b, t0) : 0;
       load_k(cs, t0, pg0);
       load_v(cs, t0, pg0);
       if constexpr (ROPE) rotate_q();
     }
-    const int t1 = t0 + 4 * BN;
+    const int t1 = t0 + WS * BN;
     // (the next tile's page is looked up before this tile's products, so the
     // scalar load has completed when the next tile's loads are issued)
     const int pg1 = PAGED && t1 < row1 ? page_of(b, t1) : 0;
     compute_tile(t0, t1 < row1 ? t1 : -1, pg1);
   }
 
-  // ---- merge the 4 waves -----------------------------------------------------------
-  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 16);  // the four lane groups of a query
   lsum += __shfl_xor(lsum, 32);
+  if constexpr (SOLO) {
+    // The wave's own result for the G query heads: lane (li < G, lg) holds
+    // output dimensions db*16 + 4*lg + r of query head li.
+    if (li < G) {
+      const size_t head = (size_t)b * Hq + (size_t)g * G + li;
+      if (cur.direct) {  // (divided as the merged form divides)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          uint32_t *dst = static_cast<uint32_t *>(outp) + (head * D + db * 16 + 4 * lg) / 2;
+          *reinterpret_cast<u32x2_t *>(dst) =
+              u32x2_t{pack_bf16x2(o[db][0] / lsum, o[db][1] / lsum),
+                      pack_bf16x2(o[db][2] / lsum, o[db][3] / lsum)};
+        }
+      } else {
+        const size_t ps = head * splits + cur.slot;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          *reinterpret_cast<f32x4_t *>(ws_o + ps * D + db * 16 + 4 * lg) = o[db];
+        if (lg == 0) *reinterpret_cast<float2 *>(ws_ml + ps * 2) = make_float2(m, lsum);
+      }
+    }
+    return;
+  } else {
+  // ---- merge the 4 waves -----------------------------------------------------------
   __syncthreads();  // every wave is done with its Vᵀ tile
   float *wm = reinterpret_cast<float *>(smem);  // [4][16]
   float *wl = wm + 4 * 16;                      // [4][16]
@@ -654,18 +696,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
   __syncthreads();
   finish<true, D, G, kThreads>(fin_m, fin_l, fo, cur.direct != 0, b, g, cur.slot, Hq,
                                splits, outp, ws_ml, ws_o);
+  }  // !SOLO
   };  // run
 
-  if (balanced) {
-    // Tiles [wg*C, min((wg+1)*C, TT)) of the batch's (b, g, tile) order.
+  if constexpr (SOLO) {
+    // Worker u = 4 * wg + w takes the tiles [u*C, min((u+1)*C, TT)) of the
+    // batch's (b, g, tile) order, P workers in all (balanced schedule).
+    // Workgroup i runs on XCD i % 8: wg = (i % 8) * (P / 32) + i / 8 gives
+    // each XCD a contiguous run of workers (P / 4 is a multiple of 8).
     const BatchTiles bt = batch_tiles(seq_lens, B, max_length, BN);
     const int TT = Hkv * bt.total;
     const int C = chunk_tiles(TT, P, C_min);
-    // workgroup i runs on XCD i % 8: chunk (i % 8) * (P / 8) + i / 8 gives
-    // each XCD a contiguous run of chunks (P is a multiple of 8)
-    const int wg = (int)(blockIdx.x % 8) * (P / 8) + (int)blockIdx.x / 8;
-    const int lo = wg * C;
-    if (lo >= TT) return;
+    const int wg = (int)(blockIdx.x % 8) * (P / 32) + (int)blockIdx.x / 8;
+    const int u = 4 * wg + w;
+    const int lo = u * C;
+    if (lo >= TT) return;  // (no workgroup barrier follows in this path)
     const int hi = min(lo + C, TT);
     // the sequence of tile lo: the first b with Hkv * (tiles up to b) > lo
     int b = 0;
@@ -686,14 +731,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     auto piece_at = [&](int from, int &end) {
       const int start = Hkv * Pb + g * nb;  // first tile of (b, g)
       const int t_end = min(nb, hi - start);
-      const int first = start / C;          // workgroup holding tile 0 of (b, g)
+      const int first = start / C;          // worker holding tile 0 of (b, g)
       Piece p;
       p.b = b;
       p.g = g;
       p.row0 = (from - start) * BN;
       p.row1 = min(t_end * BN, Lb);
       p.L = Lb;
-      p.slot = wg - first;
+      p.slot = u - first;
       p.direct = first == (start + nb - 1) / C;
       p.valid = 1;
       end = start + t_end;
@@ -716,11 +761,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
         if (nb == 0) break;  // (not reached: tiles remain, so rows do)
       }
       from = end;
-      __syncthreads();  // the next piece reuses the LDS
     }
-    return;
-  }
-
+  } else {
   const Unit un = locate_unit(seq_lens, gridDim.y, Hkv, max_length, split_rows);
   if (un.b < 0) return;
   const Item it = make_item(seq_lens, un.b, position_id, max_length, split_rows, un.s);
@@ -729,6 +771,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     return;
   }
   run(Piece{un.b, un.g, it.row0, it.row1, it.L, un.s, it.n_split == 1, 1});
+  }  // !SOLO
 }
 
 // ---------------------------------------------------------------------------
@@ -1020,11 +1063,15 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   }
 }
 
+
 template <bool BF16, int D, int G, int MODE>
 void launch_split(const DecodeArgs &a, hipStream_t stream) {
-  const dim3 grid = a.plan.balanced ? dim3(a.plan.P) : dim3(a.Hkv, a.B, a.plan.splits);
+  // (balanced: P workers, four per workgroup)
+  const dim3 grid = a.plan.balanced ? dim3(a.plan.P / 4) : dim3(a.Hkv, a.B, a.plan.splits);
   if constexpr (BF16) {
-    decode_bf16_kernel<D, G, MODE><<<grid, kThreads, 0, stream>>>(
+    auto *kern = a.plan.balanced ? decode_bf16_kernel<D, G, MODE, true>
+                                 : decode_bf16_kernel<D, G, MODE, false>;
+    kern<<<grid, kThreads, 0, stream>>>(
         static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
         static_cast<const uint16_t *>(a.v), a.seq_lens, a.position_id, a.out,
         a.ws_ml, a.ws_o, a.Hq, a.Hkv, a.max_length,
