@@ -40,10 +40,11 @@
 // group of D/4 lanes (16-byte loads), dot products reduced with DPP row
 // operations, online softmax per group.
 //
-// Both end the same way: the workgroup merges its waves / row groups and
-// either writes the output directly (the sequence has a single split) or
-// writes one partial (running max, running sum, unnormalised output) per
-// query head to the workspace. decode_combine_kernel then merges the
+// Both end the same way: the workgroup merges its waves / row groups (under
+// the balanced schedule every wave ends on its own, no merge) and either
+// writes the output directly (the sequence has a single split) or writes
+// one partial (running max, running sum, unnormalised output) per query
+// head to the workspace. decode_combine_kernel then merges the
 // partials of every multi-split sequence (log-sum-exp: each partial weighted
 // by exp of its running max less the largest), divides by the total sum and
 // casts to the output type. (Merging inside the
@@ -308,9 +309,9 @@ struct Bf16Tile {
 
 // A piece of work: rows [row0, row1) of kv head g of sequence b (valid length
 // L); direct: the piece is the whole (b, g), whose output it writes, else its
-// partial goes to slot `slot` of (b, g). valid = 0: no piece.
+// partial goes to slot `slot` of (b, g).
 struct Piece {
-  int b, g, row0, row1, L, slot, direct, valid;
+  int b, g, row0, row1, L, slot, direct;
 };
 
 // MODE: 0 = contiguous cache, 1 = contiguous cache with the fused append,
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     uint16_t *kw, uint16_t *vw, const int32_t *__restrict__ block_table,
     int max_blocks, int page_size, int num_pages, int head_major,
     const float *__restrict__ rcos, const float *__restrict__ rsin, int B,
-    int balanced, int P, int C_min) {
+    int P, int C_min) {
   constexpr bool APPEND = MODE == 1 || MODE == 3;
   constexpr bool PAGED = MODE == 2;
   constexpr bool ROPE = MODE == 3;
@@ -740,7 +741,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
       p.L = Lb;
       p.slot = u - first;
       p.direct = first == (start + nb - 1) / C;
-      p.valid = 1;
       end = start + t_end;
       return p;
     };
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     if (it.L == 0 && un.s == 0) write_zero_rows<true, D, G, kThreads>(outp, un.b, un.g, Hq);
     return;
   }
-  run(Piece{un.b, un.g, it.row0, it.row1, it.L, un.s, it.n_split == 1, 1});
+  run(Piece{un.b, un.g, it.row0, it.row1, it.L, un.s, it.n_split == 1});
   }  // !SOLO
 }
 
@@ -1079,7 +1079,7 @@ void launch_split(const DecodeArgs &a, hipStream_t stream) {
         static_cast<const uint16_t *>(a.k_new), static_cast<const uint16_t *>(a.v_new),
         static_cast<uint16_t *>(a.k_w), static_cast<uint16_t *>(a.v_w),
         a.block_table, a.max_blocks, a.page_size, a.num_pages, a.head_major,
-        a.rope_cos, a.rope_sin, a.B, a.plan.balanced, a.plan.P, a.plan.C_min);
+        a.rope_cos, a.rope_sin, a.B, a.plan.P, a.plan.C_min);
   } else {
     static_assert(MODE != 2, "paged caches are bf16 only");
     decode_f32_kernel<D, G, MODE == 1 || MODE == 3, MODE == 3><<<grid, kThreads, 0, stream>>>(
