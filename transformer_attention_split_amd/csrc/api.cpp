@@ -496,6 +496,11 @@ attn_status attn_decode_paged(attn_dtype dtype, const void *q, const void *k_pag
   a.page_size = page_size;
   a.num_pages = num_pages;
   a.head_major = page_layout == ATTN_PAGES_HEAD_MAJOR;
+  // Token-major pages keep the kv heads of a token side by side: under the
+  // balanced schedule a workgroup's four waves then take four neighbouring
+  // heads of the same tiles (the plan's C_min and slot bound hold: a quarter
+  // of the units, a quarter of the workers).
+  if (a.plan.balanced && !a.head_major && Hkv % 4 == 0) a.plan.hgs = 4;
   hipError_t e = attn::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();

@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     uint16_t *kw, uint16_t *vw, const int32_t *__restrict__ block_table,
     int max_blocks, int page_size, int num_pages, int head_major,
     const float *__restrict__ rcos, const float *__restrict__ rsin, int B,
-    int P, int C_min) {
+    int P, int C_min, int hgs) {
   constexpr bool APPEND = MODE == 1 || MODE == 3;
   constexpr bool PAGED = MODE == 2;
   constexpr bool ROPE = MODE == 3;
@@ -701,23 +701,28 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
   };  // run
 
   if constexpr (SOLO) {
-    // Worker u = 4 * wg + w takes the tiles [u*C, min((u+1)*C, TT)) of the
-    // batch's (b, g, tile) order, P workers in all (balanced schedule).
+    // Worker u takes the tiles [u*C, min((u+1)*C, TT)) of the batch's
+    // (b, h, tile) order (balanced schedule). hgs == 1: h is the kv head and
+    // every wave a worker, u = 4 * wg + w, P workers. hgs == 4 (token-major
+    // pages): h is a group of four kv heads and every workgroup a worker,
+    // u = wg, P / 4 workers; its wave w takes kv head 4h + w of every tile,
+    // so that the four waves read neighbouring slices of the same token rows.
     // Workgroup i runs on XCD i % 8: wg = (i % 8) * (P / 32) + i / 8 gives
     // each XCD a contiguous run of workers (P / 4 is a multiple of 8).
+    const int NH = Hkv / hgs;  // units h per sequence
     const BatchTiles bt = batch_tiles(seq_lens, B, max_length, BN);
-    const int TT = Hkv * bt.total;
-    const int C = chunk_tiles(TT, P, C_min);
+    const int TT = NH * bt.total;
+    const int C = chunk_tiles(TT, hgs == 1 ? P : P / 4, C_min);
     const int wg = (int)(blockIdx.x % 8) * (P / 32) + (int)blockIdx.x / 8;
-    const int u = 4 * wg + w;
+    const int u = hgs == 1 ? 4 * wg + w : wg;
     const int lo = u * C;
     if (lo >= TT) return;  // (no workgroup barrier follows in this path)
     const int hi = min(lo + C, TT);
-    // the sequence of tile lo: the first b with Hkv * (tiles up to b) > lo
+    // the sequence of tile lo: the first b with NH * (tiles up to b) > lo
     int b = 0;
 #pragma unroll
     for (int c = 0; c < kBalancedMaxB / 64; ++c) {
-      const unsigned long long hit = __ballot(Hkv * bt.incl[c] > lo);
+      const unsigned long long hit = __ballot(NH * bt.incl[c] > lo);
       if (hit != 0ull) {
         b = 64 * c + __ffsll(hit) - 1;
         break;
@@ -727,15 +732,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     int nb = seq_value(bt.cnt, b);
     int Pb = seq_value(bt.incl, b) - nb;
     int Lb = seq_value(bt.len, b);
-    int g = (lo - Hkv * Pb) / nb;
-    // the piece of (b, g) from tile `from` up to the range's end; its end tile
+    int h = (lo - NH * Pb) / nb;
+    // the piece of (b, h) from tile `from` up to the range's end; its end tile
     auto piece_at = [&](int from, int &end) {
-      const int start = Hkv * Pb + g * nb;  // first tile of (b, g)
+      const int start = NH * Pb + h * nb;   // first tile of (b, h)
       const int t_end = min(nb, hi - start);
-      const int first = start / C;          // worker holding tile 0 of (b, g)
+      const int first = start / C;          // worker holding tile 0 of (b, h)
       Piece p;
       p.b = b;
-      p.g = g;
+      p.g = hgs == 1 ? h : hgs * h + w;
       p.row0 = (from - start) * BN;
       p.row1 = min(t_end * BN, Lb);
       p.L = Lb;
@@ -748,9 +753,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
     for (;;) {
       run(piece_at(from, end));
       if (end >= hi) break;
-      // the next piece is tile 0 of the next (b, g)
-      if (++g == Hkv) {  // next sequence that holds rows
-        g = 0;
+      // the next piece is tile 0 of the next (b, h)
+      if (++h == NH) {  // next sequence that holds rows
+        h = 0;
         Pb += nb;
         nb = 0;
         while (nb == 0 && b + 1 < B) {
@@ -963,7 +968,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     const float *__restrict__ ws_ml, const float *__restrict__ ws_o,
     const int32_t *__restrict__ seq_lens, int position_id,
     void *__restrict__ outp, int Hq, int max_length, int split_rows,
-    int splits, int Hkv, int balanced, int P, int C_min) {
+    int splits, int Hkv, int balanced, int P, int C_min, int hgs) {
   constexpr int PER = D / 64;  // output dimensions per lane
   static_assert(PER == 1 || PER == 2, "D is 64 or 128");
   const int hq = blockIdx.x;
@@ -983,8 +988,9 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
       for (int e = 0; e < PER; ++e) store_out<BF16>(outp, head * D + lane * PER + e, 0.f);
       return;
     }
-    const int C = chunk_tiles(Hkv * bt.total, P, C_min);
-    const int start = Hkv * Pb + (hq / (Hq / Hkv)) * nb;
+    const int NH = Hkv / hgs;  // units per sequence
+    const int C = chunk_tiles(NH * bt.total, hgs == 1 ? P : P / 4, C_min);
+    const int start = NH * Pb + (hq / (Hq / Hkv)) / hgs * nb;
     n = (start + nb - 1) / C - start / C + 1;
   } else {
     n = make_item(seq_lens, b, position_id, max_length, split_rows, 0).n_split;
@@ -1079,7 +1085,7 @@ void launch_split(const DecodeArgs &a, hipStream_t stream) {
         static_cast<const uint16_t *>(a.k_new), static_cast<const uint16_t *>(a.v_new),
         static_cast<uint16_t *>(a.k_w), static_cast<uint16_t *>(a.v_w),
         a.block_table, a.max_blocks, a.page_size, a.num_pages, a.head_major,
-        a.rope_cos, a.rope_sin, a.B, a.plan.P, a.plan.C_min);
+        a.rope_cos, a.rope_sin, a.B, a.plan.P, a.plan.C_min, a.plan.hgs);
   } else {
     static_assert(MODE != 2, "paged caches are bf16 only");
     decode_f32_kernel<D, G, MODE == 1 || MODE == 3, MODE == 3><<<grid, kThreads, 0, stream>>>(
@@ -1112,7 +1118,7 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
   decode_combine_kernel<BF16, D><<<dim3(a.Hq, a.B), 64, 0, stream>>>(
       a.ws_ml, a.ws_o, a.seq_lens, a.position_id, a.out, a.Hq, a.max_length,
       a.plan.split_rows, a.plan.splits, a.Hkv, a.plan.balanced, a.plan.P,
-      a.plan.C_min);
+      a.plan.C_min, a.plan.hgs);
   return hipGetLastError();
 }
 

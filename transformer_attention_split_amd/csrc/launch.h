@@ -26,6 +26,9 @@ struct DecodePlan {
   // P workgroups, each at least C_min wave tiles of 4096/D rows.
   int balanced = 0;
   int P = 0, C_min = 0;
+  // kv heads per unit of the balanced order: 1, or 4 for token-major pages
+  // (a workgroup's four waves take four neighbouring heads of a tile)
+  int hgs = 1;
 };
 
 struct DecodeArgs {
