@@ -596,14 +596,23 @@ def cpu_baseline(dec, synth):
 # ----------------------------------------------------------------------------
 # HBM traffic from committed counter summaries
 # ----------------------------------------------------------------------------
-def kernel_source_hash(name):
-    path = os.path.join(ROOT, "transformer_attention_split_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(names):
+    """First 16 hex digits of the SHA-256 over the named csrc/ files, in
+    order: the kernel and the host code that plans its launch."""
+    h = hashlib.sha256()
+    for name in names:
+        path = os.path.join(ROOT, "transformer_attention_split_amd", "csrc", name)
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
-def committed_traffic(summary, source):
+# the decode kernels, their shared helpers, and the host side of the split plan
+DECODE_SOURCES = ("decode.hip", "common.h", "launch.h", "api.cpp")
+
+
+def committed_traffic(summary, sources):
     """Bytes per launch from a profiles/ summary, if it was taken on the
-    current kernel source (the summary records the source hash)."""
+    current sources (the summary records their hash)."""
     path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
@@ -612,7 +621,7 @@ def committed_traffic(summary, source):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
-    if fields.get("source_sha256_16") != kernel_source_hash(source):
+    if fields.get("source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -770,7 +779,7 @@ def main():
                "gpu_state_after": state_after}
 
     traffic = committed_traffic("decode_ragged_b64_traffic.txt",
-                                "decode.hip")
+                                DECODE_SOURCES)
     roofline = {
         "kernel": "decode_bf16_kernel<128, 4, 0, true> + decode_combine_kernel<true, 128> (one attn_decode call)",
         "bound": "hbm", "achieved": round(dec_gbps, 1),

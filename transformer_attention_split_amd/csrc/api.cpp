@@ -292,6 +292,15 @@ attn_status decode_check(const char *fn, attn_dtype dtype, const void *q, const 
       a.plan.P = bp.P;
       a.plan.C_min = bp.C_min;
       a.plan.splits = bp.S;  // pieces start at wave-tile rows: no page straddles
+      // Groups of four kv heads: a workgroup's four waves take four
+      // neighbouring heads of the same tiles (the plan's C_min and slot bound
+      // hold: a quarter of the units, a quarter of the workers). Token-major
+      // pages keep the heads of a token side by side, so the four waves read
+      // 1 KiB contiguous of the same token rows (168.3 against 184.4 us with
+      // one wave per head, ragged batch in 64-row pages); contiguous caches
+      // gain 1-2 % (ragged batch 159.3 against 160.9 us, sorted 158.5
+      // against 162.3 us), and every layout keeps one plan.
+      if (Hkv % 4 == 0) a.plan.hgs = 4;
     }
   }
   if (!a.plan.balanced && a.plan.split_rows % row_multiple != 0) {  // fewer splits: still fits
@@ -496,11 +505,6 @@ attn_status attn_decode_paged(attn_dtype dtype, const void *q, const void *k_pag
   a.page_size = page_size;
   a.num_pages = num_pages;
   a.head_major = page_layout == ATTN_PAGES_HEAD_MAJOR;
-  // Token-major pages keep the kv heads of a token side by side: under the
-  // balanced schedule a workgroup's four waves then take four neighbouring
-  // heads of the same tiles (the plan's C_min and slot bound hold: a quarter
-  // of the units, a quarter of the workers).
-  if (a.plan.balanced && !a.head_major && Hkv % 4 == 0) a.plan.hgs = 4;
   hipError_t e = attn::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();

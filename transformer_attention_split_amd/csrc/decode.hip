@@ -703,8 +703,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_bf16_kernel(
   if constexpr (SOLO) {
     // Worker u takes the tiles [u*C, min((u+1)*C, TT)) of the batch's
     // (b, h, tile) order (balanced schedule). hgs == 1: h is the kv head and
-    // every wave a worker, u = 4 * wg + w, P workers. hgs == 4 (token-major
-    // pages): h is a group of four kv heads and every workgroup a worker,
+    // every wave a worker, u = 4 * wg + w, P workers. hgs == 4 (Hkv a multiple
+    // of 4): h is a group of four kv heads and every workgroup a worker,
     // u = wg, P / 4 workers; its wave w takes kv head 4h + w of every tile,
     // so that the four waves read neighbouring slices of the same token rows.
     // Workgroup i runs on XCD i % 8: wg = (i % 8) * (P / 32) + i / 8 gives
