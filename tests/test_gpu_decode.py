@@ -175,6 +175,26 @@ def test_decode_group_sizes_and_dims(dtype, D, G):
     assert err <= tol(dtype), err
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hkv", [3, 4, 6, 12])
+def test_decode_balanced_kv_head_counts(D, Hkv):
+    # Ragged bf16 batches run the balanced schedule: with Hkv a multiple of 4
+    # a workgroup takes four neighbouring kv heads (one per wave), otherwise
+    # every wave takes one kv head of its own. Both orders on head counts that
+    # are not powers of two, with an empty sequence and runs of one tile
+    # (split_rows 1) as well as the planner's.
+    lens = np.array([1, 700, 333, 0, 64, 129])
+    inp = synth.decode_ragged(110 + Hkv, B=6, Hq=2 * Hkv, Hkv=Hkv, D=D,
+                              max_length=700, dtype="bf16", lengths=lens)
+    ref = oracle_of(inp)
+    for split_rows in (0, 1):
+        say(f"decode bf16 balanced D={D} Hkv={Hkv} split_rows={split_rows}")
+        out = to_host64(run_decode(inp, split_rows=split_rows))
+        assert np.all(out[3] == 0)
+        err = max_abs_err(out, ref)
+        assert err <= tol("bf16"), (split_rows, err)
+
+
 @pytest.mark.parametrize("split_rows", [1, 7, 64, 100, 128, 1000, 5000])
 def test_decode_split_invariance(split_rows):
     inp = synth.decode_ragged(21, B=2, Hq=8, Hkv=2, D=128, max_length=3000,
