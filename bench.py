@@ -21,14 +21,16 @@ Unless --no-secondary is given, the `secondary` object also times the fused
 append (plain and with the rotary embedding) and the paged decode on the
 decode batch, the decoder-causal top-k, the paged prefill, the prefill shape
 at head size 128 and with 32 heads, and the single-sequence decode at
-position 8000 (cold and warm, from a captured graph).
+position 8000 (cold and warm, from a captured graph; --no-single skips only
+that part).
 
 The `context` object holds the read bandwidth a compute-free streaming read
 over 4 GiB attains (attn_read_probe), against which the decode bandwidth can
 be read, and the GPU's clock levels, performance level, power and
 temperatures (sysfs) just before and after the timed steps.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-secondary | --no-single] [--calib-copy]
 """
 import argparse
 import glob
@@ -62,7 +64,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the single-sequence position-8000 figures")
+                    help="skip every secondary figure (fused append, paged "
+                         "forms, other prefill shapes, single-sequence decode)")
+    ap.add_argument("--no-single", action="store_true",
+                    help="skip only the single-sequence position-8000 figures "
+                         "(graph replays of thousands of calls)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -768,7 +774,7 @@ def main():
         secondary["prefill_paged_prefix3072"] = [
             bench_prefill_paged(torch, tas, pre, ps, lay)
             for lay in ("token", "head") for ps in (64, 256)]
-    if not args.no_secondary:
+    if not args.no_secondary and not args.no_single:
         log("single-sequence position-8000 decode (graph replay) ...")
         secondary["decode_single_pos8000"] = bench_single_position(
             torch, tas, synth)

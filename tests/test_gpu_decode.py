@@ -195,6 +195,32 @@ def test_decode_balanced_kv_head_counts(D, Hkv):
         assert err <= tol("bf16"), (split_rows, err)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_decode_balanced_random_batches(seed):
+    # Seeded random batch compositions for the balanced schedule's work
+    # order (runs crossing sequence and kv-head ends, slots, the combine's
+    # recount of the pieces): batch size, kv heads, group size, head size,
+    # lengths with zeros and full rows, and the least run length.
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.choice([2, 3, 5, 17, 64, 100, 256]))
+    Hkv = int(rng.choice([1, 2, 3, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    M = int(rng.integers(1, 700))
+    lens = rng.integers(0, M + 1, B).astype(np.int32)
+    lens[rng.random(B) < 0.1] = 0
+    lens[rng.random(B) < 0.1] = M
+    split_rows = int(rng.choice([0, 1, 33, 64, 257]))
+    inp = synth.decode_ragged(2000 + seed, B=B, Hq=G * Hkv, Hkv=Hkv, D=D,
+                              max_length=M, dtype="bf16", lengths=lens)
+    say(f"decode bf16 balanced random seed={seed} B={B} Hkv={Hkv} G={G} "
+        f"D={D} M={M} split_rows={split_rows}")
+    out = to_host64(run_decode(inp, split_rows=split_rows))
+    assert np.all(out[lens == 0] == 0)
+    err = max_abs_err(out, oracle_of(inp))
+    assert err <= tol("bf16"), err
+
+
 @pytest.mark.parametrize("split_rows", [1, 7, 64, 100, 128, 1000, 5000])
 def test_decode_split_invariance(split_rows):
     inp = synth.decode_ragged(21, B=2, Hq=8, Hkv=2, D=128, max_length=3000,

@@ -14,9 +14,11 @@
 //     K and V operand feeds two products) x key quarter kq = w % 4 (tiles t
 //     with t % 4 == kq). Two waves per SIMD. The four key quarters of a query
 //     group are merged (log-sum-exp) in LDS at the end.
-//   * Block -> work map: workgroup id i runs on XCD i % 8; every query tile of
-//     one head goes to the same XCD, so the head's K and V are fetched from
-//     HBM once into that XCD's L2; on each XCD tiles run longest first.
+//   * Block -> work map: workgroup id i runs on XCD i % 8; each XCD takes a
+//     contiguous run of head instances, so every query tile of a head, and
+//     every query head of a kv head (grouped-query attention), reads that kv
+//     head's K and V through the same L2, fetched from HBM about once; on
+//     each XCD tiles run longest first.
 //   * Each iteration's four K tiles and four V tiles cross the L1 path once
 //     per workgroup, as buffer loads that write LDS directly, double-buffered,
 //     one workgroup barrier per iteration; the next iteration's loads are
@@ -163,7 +165,10 @@ __global__ __launch_bounds__(P64::THREADS) void prefill_lds_kernel(
   const int id = blockIdx.x;
   const int xcd = id % kXcds;
   const int k = id / kXcds;
-  const int j = xcd + kXcds * (k % heads_per_xcd);  // head instance b*Hq + h
+  // XCD x takes head instances [x * heads_per_xcd, (x + 1) * heads_per_xcd):
+  // consecutive query heads share a kv head, so a kv head's K and V are
+  // fetched into one L2 for all the query heads that read them
+  const int j = xcd * heads_per_xcd + k % heads_per_xcd;  // head instance b*Hq + h
   if (j >= NH) return;
   // (integer division runs on the vector ALUs; readfirstlane keeps the
   // workgroup-uniform results in scalar registers)
