@@ -76,6 +76,38 @@ def test_prefill_shapes(D, B, Hq, Hkv, Lq, prefix, extra):
     assert err <= tol("bf16"), err
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_prefill_random_shapes(seed):
+    # Seeded random shapes across the kernel forms (D 64 and 128; grids of
+    # one and of two or more workgroups per CU; GQA groups; prefixes on and
+    # off the key tile; ragged last query tiles), sized so the oracle stays
+    # fast (at most 5e7 visible (query, key) pairs per head group).
+    rng = np.random.default_rng(4000 + seed)
+    while True:
+        B = int(rng.choice([1, 2, 3]))
+        Hkv = int(rng.choice([1, 2, 3, 4, 8]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        D = int(rng.choice([64, 128]))
+        Lq = int(rng.integers(1, 700))
+        prefix = int(rng.choice([0, 64, 128, int(rng.integers(1, 1200))]))
+        if seed % 2 == 0:  # grids of two or more workgroups per CU (>= 768)
+            Hkv = int(rng.choice([2, 4, 8]))
+            Hq = 64
+            B = 3
+            Lq = int(rng.integers(200, 400))
+            prefix = int(rng.integers(0, 200))
+        pairs = B * Hq * Lq * (prefix + Lq)
+        if pairs <= 5e7:
+            break
+    extra = int(rng.integers(0, 50))
+    inp = synth.prefill(5000 + seed, B, Hq, Hkv, D, Lq, prefix,
+                        max_length=prefix + Lq + extra, dtype="bf16")
+    say(f"prefill random seed={seed} D={D} B={B} Hq={Hq} Hkv={Hkv} Lq={Lq} "
+        f"prefix={prefix} extra={extra}")
+    err = max_abs_err(to_host64(run(inp)), oracle_of(inp))
+    assert err <= tol("bf16"), err
+
+
 def test_prefill_row_equals_decode_at_prefix_plus_i():
     inp = synth.prefill(31, 1, 8, 2, 128, 70, 150, dtype="bf16")
     q, k, v = dev_inputs(inp)
