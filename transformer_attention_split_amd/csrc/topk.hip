@@ -35,7 +35,8 @@
 //   3. gather: lanes = 4 slot groups x 16 groups of 4 dimensions; each slot
 //      group walks every 4th selected key and adds score * v[key] in fp64
 //      (one coalesced 256-byte row read per key per slot group, 16 in flight);
-//      the four partial sums are added across lanes and rounded to fp32.
+//      the four partial sums are added across the lane rows in registers
+//      (permlane swaps) and rounded to fp32.
 #include <type_traits>
 
 #include "common.h"
@@ -81,6 +82,24 @@ __device__ __forceinline__ float wave_extreme(float x) {
   x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// x of this lane plus x of lane l ^ 16 (ROW2 false) or l ^ 32 (true): the
+// 16-lane rows of the wave swapped in registers (v_permlane16_swap /
+// v_permlane32_swap on both 32-bit halves), no LDS round trip. The swap
+// hands each lane the pair {x_l, x_partner} in either order; the sum is the
+// same either way.
+template <bool ROW2>
+__device__ __forceinline__ double add_row_partner(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  const auto a = ROW2 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                      : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto c = ROW2 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                      : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const double d0 = __longlong_as_double((long long)(((uint64_t)c[0] << 32) | a[0]));
+  const double d1 = __longlong_as_double((long long)(((uint64_t)c[1] << 32) | a[1]));
+  return d0 + d1;
 }
 
 __device__ __forceinline__ uint64_t order64(double x) {
@@ -303,8 +322,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
           }
           const uint64_t last = __ballot(l < nc && rank == need - 1);
           const int Ll = __ffsll((unsigned long long)last) - 1;
-          const double ts = __shfl(my_s, Ll);
-          const int tj = __shfl(my_j, Ll);
+          // (Ll is the same in every lane: lane reads, no LDS round trip)
+          const double ts = __longlong_as_double(
+              (long long)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(my_hi, Ll) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane(my_lo, Ll)));
+          const int tj = __builtin_amdgcn_readlane(my_j, Ll);
 #pragma unroll
           for (int t = 0; t < NTP; ++t)
             selm[t] |= __ballot(((cm[t] >> l) & 1ull) &&
@@ -409,8 +431,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(
       if (p0 < cnt) chunk(p0, std::false_type{});
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[e] += __shfl_xor(acc[e], 16);
-        acc[e] += __shfl_xor(acc[e], 32);
+        acc[e] = add_row_partner<false>(acc[e]);
+        acc[e] = add_row_partner<true>(acc[e]);
       }
       if (sg == 0) {
         const float4 o = {(float)acc[0], (float)acc[1], (float)acc[2], (float)acc[3]};
