@@ -55,11 +55,14 @@ bool fits(std::initializer_list<double> dims) {
 // that is a whole number of rounds of the workgroup's four wave tiles (one
 // wave tile is 8 KiB of K: 4096/D rows). At most attn::kDecodeMaxSplits
 // splits per sequence: a smaller forced split_rows is raised to
-// ceil(max_length / kDecodeMaxSplits). The target was measured on 64
-// uniformly ragged sequences of up to 8192 rows (Hkv 8, D 128), where it gives
-// 896-row splits: 165 us per call against 169 us at 768 rows and 171 us at
-// 1024 rows (fewer, longer splits leave a longer tail; more, shorter ones
-// pay more per-workgroup start-up and combine work).
+// ceil(max_length / kDecodeMaxSplits). This plain grid runs fp32 caches,
+// single sequences, batches without per-sequence lengths and batches of more
+// than kBalancedMaxB sequences. The target was measured on 64 uniformly
+// ragged sequences of up to 8192 rows (Hkv 8, D 128; before those went to the
+// balanced schedule below), where it gives 896-row splits: 165 us per call
+// against 169 us at 768 rows and 171 us at 1024 rows (fewer, longer splits
+// leave a longer tail; more, shorter ones pay more per-workgroup start-up
+// and combine work).
 // ---------------------------------------------------------------------------
 constexpr long kTargetBlocks = 5120;
 constexpr long kCUs = 256;  // compute units of an MI355X
@@ -108,7 +111,10 @@ attn::DecodePlan plan_decode(int B, int Hkv, int D, int max_length,
 // the device side is described in decode.hip). Every wave is a worker that
 // streams an equal run of the batch's wave tiles (at least C_min of them),
 // across sequence ends, and writes one partial per piece it cuts: no merge
-// of waves, no workgroup barrier. Two workgroups per CU, the split kernel's
+// of waves, no workgroup barrier. (With Hkv a multiple of 4 the unit is a
+// group of four kv heads and the workgroup the worker, its wave w on head
+// 4h + w: a quarter of the units for a quarter of the workers, so the same
+// C_min and slot bound hold.) Two workgroups per CU, the split kernel's
 // occupancy, so that every worker is resident from start to end: P = 4 *
 // 512 workers (fewer when the batch at full length holds fewer runs of
 // C_min tiles; P / 4 a multiple of 8, the XCD count, each of which takes a
