@@ -128,8 +128,9 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int D,
  *              1024 splits per sequence: a smaller value is raised to
  *              ceil(max_length / 1024). For bf16 with seq_lens and
  *              2 <= B <= 256 the work is balanced over the launch instead:
- *              every workgroup takes an equal run of the batch's rows,
- *              across sequence ends, and split_rows is the least run
+ *              every wave (with Hkv a multiple of 4, every workgroup, over
+ *              four neighbouring kv heads) takes an equal run of the batch's
+ *              rows, across sequence ends, and split_rows is the least run
  *              (rounded up to whole wave tiles of 4096 / D rows).
  *   workspace  device scratch of at least
  *              attn_decode_workspace_bytes(B,Hq,Hkv,D,max_length,split_rows)
