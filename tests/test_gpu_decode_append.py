@@ -96,6 +96,30 @@ def test_append_ragged_with_empty_sequences(dtype, D, split_rows):
     check_append(inp, kn, vn, split_rows=split_rows)
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_append_random_batches(seed):
+    # Seeded random batch sizes (balanced schedule and plain grid), head
+    # counts, dtypes and least run lengths: the caches and the output equal
+    # copy + decode bit for bit, and the oracle within the tolerance.
+    rng = np.random.default_rng(92000 + seed)
+    B = int(rng.choice([1, 2, 5, 64, 100, 300]))
+    Hkv = int(rng.integers(1, 9))
+    G = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    M = int(rng.integers(1, 700))
+    dt = "f32" if rng.random() < 0.25 else "bf16"
+    sr = int(rng.choice([0, 1, 64]))
+    lens = rng.integers(0, M + 1, B).astype(np.int32)
+    lens[rng.random(B) < 0.1] = 0
+    lens[rng.random(B) < 0.1] = M
+    inp = synth.decode_ragged(93000 + seed, B=B, Hq=G * Hkv, Hkv=Hkv, D=D,
+                              max_length=M, dtype=dt, lengths=lens)
+    kn, vn = synth.new_token_kv(93000 + seed, B, Hkv, D, dt)
+    say(f"decode_append random seed={seed} B={B} Hkv={Hkv} G={G} D={D} M={M} "
+        f"{dt} split_rows={sr}")
+    check_append(inp, kn, vn, split_rows=sr)
+
+
 def test_append_ragged_batch_over_reorder_limit():
     # more than 256 sequences: the plain grid order instead of the on-device
     # work map

@@ -50,6 +50,49 @@ def test_paged_ragged_with_empty_sequences(D, page_size, G, layout):
     assert err <= tol("bf16"), err
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_paged_random_batches(seed):
+    # Seeded random page sizes, page counts, layouts, batch sizes (balanced
+    # schedule and plain grid), head counts and least run lengths, against
+    # the oracle. Bitwise equal to the contiguous decode wherever the two
+    # plans coincide: balanced batches, or splits already whole wave tiles
+    # (the plain grid otherwise rounds paged splits up to whole tiles, so
+    # that no tile straddles a page).
+    rng = np.random.default_rng(94000 + seed)
+    D = int(rng.choice([64, 128]))
+    tile = 4096 // D
+    ps = tile * int(rng.choice([1, 2, 4]))
+    M = ps * int(rng.integers(1, 9))
+    B = int(rng.choice([1, 2, 9, 64, 256, 260]))
+    Hkv = int(rng.integers(1, 9))
+    G = int(rng.choice([1, 2, 4, 8]))
+    layout = str(rng.choice(["token", "head"]))
+    sr = int(rng.choice([0, 1, 100, tile]))
+    lens = rng.integers(0, M + 1, B).astype(np.int32)
+    lens[rng.random(B) < 0.1] = 0
+    lens[rng.random(B) < 0.1] = M
+    inp = synth.decode_ragged(95000 + seed, B=B, Hq=G * Hkv, Hkv=Hkv, D=D,
+                              max_length=M, dtype="bf16", lengths=lens)
+    kp, vp, table = synth.paginate(inp.k_cache, inp.v_cache, ps, 95000 + seed,
+                                   layout=layout)
+    say(f"decode_paged random seed={seed} B={B} Hkv={Hkv} G={G} D={D} "
+        f"page_size={ps} M={M} {layout}-major split_rows={sr}")
+    a = run_paged(inp, kp, vp, table, split_rows=sr, layout=layout)
+    sl = torch.from_numpy(lens).cuda()
+    b = tas.attn_decode(to_dev(inp.q, "bf16"), to_dev(inp.k_cache, "bf16"),
+                        to_dev(inp.v_cache, "bf16"), seq_lens=sl,
+                        scale=inp.scale, split_rows=sr)
+    torch.cuda.synchronize()
+    if 2 <= B <= 256 or sr % tile == 0:
+        assert torch.equal(a, b)
+    ref = oracle.decode(synth.as_f32(inp.q, "bf16"),
+                        synth.as_f32(inp.k_cache, "bf16"),
+                        synth.as_f32(inp.v_cache, "bf16"), seq_lens=lens,
+                        scale=inp.scale)
+    err = max_abs_err(to_host64(a), ref)
+    assert err <= tol("bf16"), err
+
+
 @pytest.mark.parametrize("split_rows", [0, 128, 640])
 @pytest.mark.parametrize("layout", ["token", "head"])
 def test_paged_equals_contiguous_bitwise(split_rows, layout):
