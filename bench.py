@@ -18,8 +18,8 @@ bf16 rounded to nearest even), generated once and resident in HBM before the
 timed region starts.
 
 Unless --no-secondary is given, the `secondary` object also times the fused
-append (plain and with the rotary embedding) and the paged decode on the
-decode batch, the decoder-causal top-k, the paged prefill, the prefill shape
+append (plain and with the rotary embedding), the paged decode and the
+fp32 decode on the decode batch, the decoder-causal top-k, the paged prefill, the prefill shape
 at head size 128 and with 32 heads, and the single-sequence decode at
 position 8000 (cold and warm, from a captured graph; --no-single skips only
 that part).
@@ -271,6 +271,36 @@ def bench_append(torch, tas, dec, steps):
                 us_p50_decode=round(td, 2),
                 GBps_append_decode=round(dec["bytes"] / (ta * 1e-6) / 1e9, 1),
                 GBps_rope_append_decode=round(dec["bytes"] / (tr * 1e-6) / 1e9, 1))
+
+
+def bench_decode_f32(torch, tas, dec, steps):
+    """The ragged decode batch with fp32 caches (the bf16 values upcast, so
+    twice the bytes): the vector-ALU kernel on the plain split grid, HIP
+    events around each call."""
+    import numpy as np
+    p = dec["p"]
+    q, k, v = dec["q"].float(), dec["k"].float(), dec["v"].float()
+    out = torch.empty_like(q)
+    kw = dict(seq_lens=dec["seq_lens"], scale=p["scale"], out=out,
+              workspace=dec["ws"])
+    for _ in range(3):
+        tas.attn_decode(q, k, v, **kw)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+          for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        tas.attn_decode(q, k, v, **kw)
+        e[1].record()
+    torch.cuda.synchronize()
+    t = float(np.median([e[0].elapsed_time(e[1]) * 1e3 for e in ev]))
+    nbytes = 2 * dec["bytes"]
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    gbps = nbytes / (t * 1e-6) / 1e9
+    return dict(workload="decode_ragged_b64 with fp32 caches",
+                us_p50=round(t, 2), bytes=nbytes, GBps=round(gbps, 1),
+                frac_of_hbm_peak=round(gbps / HBM_PEAK_GBPS, 4))
 
 
 def bench_paged(torch, tas, dec, steps, page_size, layout):
@@ -759,6 +789,9 @@ def main():
         log("fused append + decode on the ragged batch ...")
         secondary["decode_append_ragged_b64"] = bench_append(torch, tas, dec,
                                                              args.steps)
+        log("fp32 decode on the ragged batch ...")
+        secondary["decode_f32_ragged_b64"] = bench_decode_f32(torch, tas, dec,
+                                                              args.steps)
         log("paged decode on the ragged batch ...")
         secondary["decode_paged_ragged_b64"] = [
             bench_paged(torch, tas, dec, args.steps, ps, lay)
