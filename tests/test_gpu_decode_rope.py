@@ -127,6 +127,35 @@ def test_rope_append_ragged_with_empty_sequences(dtype, D, Hq, Hkv, split_rows):
     check_rope(inp, kn, vn, cos, sin, split_rows=split_rows)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_rope_append_random_batches(seed):
+    # Seeded random batch sizes (balanced schedule and plain grid), head
+    # counts, dtypes, least run lengths and table kinds (standard angles of
+    # each sequence's row, or arbitrary values that exercise every product).
+    rng = np.random.default_rng(94000 + seed)
+    B = int(rng.choice([1, 2, 5, 64, 100, 300]))
+    Hkv = int(rng.integers(1, 9))
+    G = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    M = int(rng.integers(1, 700))
+    dt = "f32" if rng.random() < 0.25 else "bf16"
+    sr = int(rng.choice([0, 1, 64]))
+    lens = rng.integers(0, M + 1, B).astype(np.int32)
+    lens[rng.random(B) < 0.1] = 0
+    lens[rng.random(B) < 0.1] = M
+    inp = synth.decode_ragged(95000 + seed, B=B, Hq=G * Hkv, Hkv=Hkv, D=D,
+                              max_length=M, dtype=dt, lengths=lens)
+    kn, vn = synth.new_token_kv(95000 + seed, B, Hkv, D, dt)
+    if rng.random() < 0.5:
+        cos, sin = rope_tables(_rows(inp), D)
+    else:
+        cos = rng.standard_normal((B, D)).astype(np.float32)
+        sin = rng.standard_normal((B, D)).astype(np.float32)
+    say(f"decode_append_rope random seed={seed} B={B} Hkv={Hkv} G={G} D={D} "
+        f"M={M} {dt} split_rows={sr}")
+    check_rope(inp, kn, vn, cos, sin, split_rows=sr)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_rope_identity_tables_equal_the_plain_append(dtype):
     lens = np.array([3, 700, 1, 4096, 2048], np.int32)

@@ -88,6 +88,23 @@ def test_topk_causal_sizes(n, topk):
     check(inp.q, inp.k, inp.v, topk, out, idx)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_causal_random_shapes(seed):
+    # Seeded random (b, h, n, topk) across the row-length classes of the
+    # kernel (one to sixteen 64-key slots per lane), with topk from 1 to n so
+    # that dense rows, the recent-key split and the score selection all meet
+    # row tiles of every length.
+    rng = np.random.default_rng(8000 + seed)
+    b = int(rng.choice([1, 2, 3]))
+    h = int(rng.choice([1, 2, 3]))
+    n = int(rng.choice([int(rng.integers(1, 1025)), 64, 65, 128, 1023, 1024]))
+    topk = int(rng.choice([1, 2, 3, int(rng.integers(1, n + 1)), min(n, 64), n]))
+    inp = synth.topk(9000 + seed, b, h, n, 64, topk)
+    say(f"topk_causal random seed={seed} b={b} h={h} n={n} topk={topk}")
+    out, idx = run(inp.q, inp.k, inp.v, inp.topk)
+    check(inp.q, inp.k, inp.v, inp.topk, out, idx)
+
+
 def test_topk_causal_k_equals_n_is_lower_triangular():
     inp = synth.topk(150, 1, 3, 200, 64, 200)
     say("topk_causal k=n")
