@@ -94,6 +94,39 @@ def test_prefill_paged_shapes(D, layout, B, Hq, Hkv, Lq, prefix, extra, ps):
     check_paged(inp, ps, layout, 82 + Lq)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_prefill_paged_random_shapes(seed):
+    # Seeded random shapes across the kernel forms (D 64 and 128; grids of
+    # one and of two or more workgroups per CU; GQA groups; prefixes on and
+    # off the key tile; ragged last query tiles), page sizes of one to six
+    # key tiles and both page layouts: bit for bit against the contiguous
+    # prefill and within the tolerance of the oracle.
+    rng = np.random.default_rng(96000 + seed)
+    while True:
+        B = int(rng.choice([1, 2, 3]))
+        Hkv = int(rng.choice([1, 2, 3, 4, 8]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        D = int(rng.choice([64, 128]))
+        Lq = int(rng.integers(1, 700))
+        prefix = int(rng.choice([0, 64, 128, int(rng.integers(1, 1200))]))
+        if seed % 2 == 0:  # grids of two or more workgroups per CU (>= 768)
+            Hkv = int(rng.choice([2, 4, 8]))
+            Hq = 64
+            B = 3
+            Lq = int(rng.integers(200, 400))
+            prefix = int(rng.integers(0, 200))
+        if B * Hq * Lq * (prefix + Lq) <= 5e7:
+            break
+    extra = int(rng.integers(0, 50))
+    ps = (4096 // D) * int(rng.integers(1, 7))
+    layout = "token" if rng.random() < 0.5 else "head"
+    inp = synth.prefill(97000 + seed, B, Hq, Hkv, D, Lq, prefix,
+                        max_length=prefix + Lq + extra, dtype="bf16")
+    say(f"prefill_paged random seed={seed} D={D} B={B} Hq={Hq} Hkv={Hkv} "
+        f"Lq={Lq} prefix={prefix} extra={extra} page={ps} {layout}")
+    check_paged(inp, ps, layout, 97000 + seed)
+
+
 def test_prefill_paged_clamped_and_shared_pages():
     # entries past the last page or negative are clamped; two sequences may
     # share pages (a common prefix). Every page holds finite rows (no spare
